@@ -1,0 +1,83 @@
+"""Seeded synthetic inputs: the only code shared by the tests, the oracle
+checks and the benchmark.  It holds none of the attention arithmetic.
+
+Recipe (CPU, deterministic; torch's Philox-free CPU generator):
+
+* Q, K, V: ``torch.randn`` float32 ``[B, H, N, d]`` drawn in that order from
+  ``torch.Generator("cpu").manual_seed(seed)``, then cast to bfloat16.
+* Outlier inputs (the FP8 workload): for each of Q, K, V in that order,
+  before the bf16 cast, a mask ``rand < 1e-3`` picks about 0.1 % of the
+  entries, which are replaced by ``10 * randn`` (N(0, 10^2)), all drawn from
+  the same generator.  The pages' FP8 error study uses a synthetic
+  distribution with a few large outliers without giving its parameters.
+* Rotation signs: ``[H, d]`` int8 of +-1 from ``randint(0, 2) * 2 - 1`` with
+  ``Generator("cpu").manual_seed(seed + 1)``.
+* softmax_scale = 1/sqrt(d) as a float32.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+__all__ = ["make_qkv", "make_signs", "softmax_scale", "Workload", "WORKLOADS", "sweep_workloads", "sweep_seed"]
+
+
+def make_qkv(B: int, H: int, N: int, d: int, seed: int, outliers: bool = False, outlier_frac: float = 1e-3,
+             outlier_std: float = 10.0):
+    """Return bf16 CPU tensors ``(q, k, v)`` of shape ``[B, H, N, d]``."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    xs = [torch.randn((B, H, N, d), generator=g, dtype=torch.float32) for _ in range(3)]
+    if outliers:
+        for x in xs:
+            m = torch.rand(x.shape, generator=g) < outlier_frac
+            x[m] = outlier_std * torch.randn(int(m.sum()), generator=g)
+    return tuple(x.to(torch.bfloat16) for x in xs)
+
+
+def make_signs(H: int, d: int, seed: int) -> torch.Tensor:
+    """Per-head random +-1 vectors, int8 ``[H, d]``."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    return (torch.randint(0, 2, (H, d), generator=g) * 2 - 1).to(torch.int8)
+
+
+def softmax_scale(d: int) -> float:
+    """1/sqrt(d) rounded to float32 (the value passed across the C ABI)."""
+    return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())
+
+
+def sweep_seed(N: int, d: int) -> int:
+    return 73000 + 100 * (int(math.log2(d)) - 5) + int(math.log2(N))
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: tuple = (False,)
+    seed: int = 0
+    outliers: bool = False
+    fp8: bool = False
+    notes: str = field(default="", compare=False)
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 1, 128, 64, (False,), 73001),
+    "std": Workload("std", 4, 16, 2048, 128, (False, True), 73002),
+    "long": Workload("long", 1, 16, 65536, 128, (True,), 73400),
+    "fp8": Workload("fp8", 4, 16, 4096, 128, (False,), 73500, outliers=True, fp8=True),
+}
+
+
+def sweep_workloads():
+    """Sequence-length sweep at 16384 total tokens and hidden size 2048."""
+    out = []
+    for d in (64, 128, 256):
+        for N in (512, 1024, 2048, 4096, 8192, 16384):
+            out.append(Workload(f"sweep_d{d}_N{N}", 16384 // N, 2048 // d, N, d, (False, True), sweep_seed(N, d)))
+    return out

@@ -1,0 +1,227 @@
+"""FP8 E4M3 emulation: codec, Hadamard rotation, block scales, FP8 attention.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): the product path never
+imports this module.
+
+What the pages fix, and the readings taken where they are silent:
+
+* Format: E4M3 with largest finite magnitude 448 (P2 section 三.3 names
+  X_max = 448 for E4M3).  The encoding is the OCP "e4m3fn" one: 1 sign bit,
+  4 exponent bits with bias 7, 3 mantissa bits, no infinities, S.1111.111 is
+  NaN, subnormals m * 2^-9.  Rounding is to nearest, ties to even, after
+  clamping to +-448 (the pages say nothing about rounding or overflow).
+* Block quantisation: one scale per block of 128 consecutive rows of one
+  (batch, head), all of d (P1 section "Block Quantization 为什么优于
+  Per-Tensor Scale" keeps one scale per B_r x d or B_c x d tile; the block
+  height of 128 is the plain choice for tiles of 128 query rows).  The scale
+  formula was lost from the page text; s = amax / 448, and s = 1 for an
+  all-zero block.  Per-tensor mode uses one amax over the whole tensor (the
+  same section's baseline, one scale for all of Q).
+* Incoherent processing: Q and K are both multiplied by the same random
+  orthogonal matrix M = diag(sigma) H_d / sqrt(d), sigma a per-head vector of
+  +-1 and H_d the Sylvester Hadamard matrix (P1 section "Incoherent
+  Processing 如何摊平离群值": random +-1 diagonal times Hadamard, so
+  (QM)(KM)^T = QK^T in exact arithmetic).  V is not rotated (P1 section
+  "为什么 V 不使用同样的 Q/K 成对抵消").
+* FP8 attention: S = scale * Q^ K^T on the dequantised operands; both GEMM
+  operands are FP8 while the softmax state stays fp32/fp64 (P1 section
+  "FP8 Attention 仍然不等于 FP8 全链路").  The probabilities that enter the PV
+  product are quantised as E4M3(P * 2^8) * 2^-8 with P = exp(S - m) in (0, 1];
+  the row sum l is taken from the unquantised P.  PARITY UNPINNED: the pages
+  never say how P is brought into FP8; the 2^8 pre-scale (exact, keeps P <=
+  256 < 448 and moves small probabilities out of the subnormal range) is this
+  build's reading.  It is pinned only in the sense that with quantisation
+  switched off the emulation equals :func:`oracle.attention.attention_ref`.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import to_f64, scale_f64
+
+__all__ = [
+    "E4M3_MAX",
+    "e4m3_decode",
+    "e4m3_encode",
+    "e4m3_round",
+    "hadamard_matrix",
+    "rotation_matrix",
+    "quantize_fp8",
+    "dequantize_fp8",
+    "fp8_attention_emulate",
+    "fp8_emulate",
+]
+
+E4M3_MAX = 448.0  # P2 section 三.3
+SCALE_BLOCK = 128  # rows per scale block
+P_PRESCALE = 256.0  # 2^8, see module docstring (parity unpinned)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of each E4M3 (e4m3fn) byte, from its bit fields."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+# the 127 non-negative finite magnitudes, in code order (monotone increasing)
+_POS_CODES = np.arange(0, 127, dtype=np.uint8)
+_POS_VALS = e4m3_decode(_POS_CODES)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3 code, ties to even, after clamping to +-448; NaN -> 0x7F.
+
+    The sign bit is kept for values that round to zero (IEEE-style -0).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    neg = np.signbit(x)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    a_safe = np.where(np.isnan(a), 0.0, a)
+    hi = np.searchsorted(_POS_VALS, a_safe, side="left")  # vals[hi-1] < a <= vals[hi]
+    hi = np.minimum(hi, 126)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a_safe - _POS_VALS[lo]
+    d_hi = _POS_VALS[hi] - a_safe
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(a_safe == _POS_VALS[hi], hi, np.where(pick_hi, hi, lo)).astype(np.uint8)
+    code = np.where(neg, code | 0x80, code).astype(np.uint8)
+    code = np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+    return code
+
+
+def e4m3_round(x) -> np.ndarray:
+    """x rounded to the nearest E4M3 value (clamped), as float64."""
+    return e4m3_decode(e4m3_encode(x))
+
+
+def hadamard_matrix(d: int) -> np.ndarray:
+    """Sylvester Hadamard matrix H_d (entries +-1): H_1 = [1],
+    H_2k = [[H_k, H_k], [H_k, -H_k]].  d must be a power of two."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    Hm = np.ones((1, 1), dtype=np.int64)
+    while Hm.shape[0] < d:
+        Hm = np.block([[Hm, Hm], [Hm, -Hm]])
+    return Hm
+
+
+def rotation_matrix(signs) -> np.ndarray:
+    """M = diag(sigma) H_d / sqrt(d) for a +-1 vector sigma (orthogonal)."""
+    s = np.asarray(signs, dtype=np.float64).reshape(-1)
+    d = s.shape[0]
+    return (s[:, None] * hadamard_matrix(d)) / np.sqrt(d)
+
+
+def _rotate(x: np.ndarray, signs) -> np.ndarray:
+    """y[b, h] = x[b, h] @ M_h with one rotation per head."""
+    signs = np.asarray(signs)
+    y = np.empty_like(x)
+    for h in range(x.shape[1]):
+        y[:, h] = x[:, h] @ rotation_matrix(signs[h])
+    return y
+
+
+def quantize_fp8(x, signs=None, per_tensor: bool = False, block: int = SCALE_BLOCK, quantize: bool = True):
+    """Rotate (optionally), scale and round one tensor ``[B, H, N, d]`` to E4M3.
+
+    Returns ``(codes, scale, y)``:
+      codes uint8 ``[B, H, N, d]`` (None when ``quantize`` is False),
+      scale float64 ``[B, H, ceil(N / block)]`` with x_hat = decode(codes) * s,
+      y the rotated (or copied) float64 tensor before quantisation.
+    """
+    x = to_f64(x)
+    B, H, N, d = x.shape
+    y = _rotate(x, signs) if signs is not None else x.copy()
+    nb = -(-N // block)
+    scale = np.empty((B, H, nb))
+    if per_tensor:
+        a = np.abs(y).max() if y.size else 0.0
+        scale[:] = a / E4M3_MAX if a > 0 else 1.0
+    else:
+        for i in range(nb):
+            a = np.abs(y[:, :, i * block:(i + 1) * block, :]).max(axis=(2, 3))
+            scale[:, :, i] = np.where(a > 0, a / E4M3_MAX, 1.0)
+    if not quantize:
+        return None, scale, y
+    s_rows = np.repeat(scale, block, axis=2)[:, :, :N, None]
+    codes = e4m3_encode(np.clip(y / s_rows, -E4M3_MAX, E4M3_MAX))
+    return codes, scale, y
+
+
+def dequantize_fp8(codes, scale, block: int = SCALE_BLOCK) -> np.ndarray:
+    """decode(codes) * s per 128-row block, float64 ``[B, H, N, d]``."""
+    N = codes.shape[2]
+    s_rows = np.repeat(np.asarray(scale, dtype=np.float64), block, axis=2)[:, :, :N, None]
+    return e4m3_decode(codes) * s_rows
+
+
+def fp8_attention_emulate(qh, kh, vh, causal: bool = False, scale=None, Bc: int = 64, quantize_p: bool = True):
+    """Online-softmax attention on already dequantised FP8 operands.
+
+    ``qh, kh, vh`` are float64 ``[B, H, N, d]`` holding exactly the values the
+    FP8 codes times their scales represent.  The recurrence is the one of
+    :func:`oracle.attention.online_ref` with key blocks of ``Bc`` rows (the
+    block size matters here: it decides the running max each probability is
+    quantised against).  With ``quantize_p`` the PV product uses
+    E4M3(P * 2^8) * 2^-8 while ``l`` sums the unquantised P.
+    """
+    qh, kh, vh = to_f64(qh), to_f64(kh), to_f64(vh)
+    B, H, N, d = qh.shape
+    Nk = kh.shape[2]
+    sc = scale_f64(scale, d)
+    qi = np.arange(N)
+    o = np.empty((B, H, N, vh.shape[3]))
+    lse = np.empty((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            m = np.full(N, -np.inf)
+            l = np.zeros(N)
+            acc = np.zeros((N, vh.shape[3]))
+            for j0 in range(0, Nk, Bc):
+                j1 = min(j0 + Bc, Nk)
+                S = sc * (qh[b, h] @ kh[b, h, j0:j1].T)
+                if causal:
+                    S = np.where(np.arange(j0, j1)[None, :] > qi[:, None], -np.inf, S)
+                m_new = np.maximum(m, S.max(axis=1))
+                dead = np.isneginf(m_new)
+                safe = np.where(dead, 0.0, m_new)
+                alpha = np.where(dead, 1.0, np.exp(m - safe))
+                P = np.where(dead[:, None], 0.0, np.exp(S - safe[:, None]))
+                l = alpha * l + P.sum(axis=1)
+                Pq = e4m3_round(P * P_PRESCALE) / P_PRESCALE if quantize_p else P
+                acc = alpha[:, None] * acc + Pq @ vh[b, h, j0:j1]
+                m = m_new
+            o[b, h] = acc / l[:, None]
+            lse[b, h] = m + np.log(l)
+    return o, lse
+
+
+def fp8_emulate(q, k, v, signs=None, mode: str = "block+had", causal: bool = False, scale=None, Bc: int = 64,
+                quantize: bool = True):
+    """End-to-end FP8 attention emulation in one of three scaling modes.
+
+    mode:
+      ``"block+had"`` -- rotate Q and K by diag(signs[h]) H_d / sqrt(d), then
+      per-block scales for Q, K and V (the product path);
+      ``"block"`` -- per-block scales, no rotation;
+      ``"tensor"`` -- one scale per tensor, no rotation (the baseline).
+    With ``quantize=False`` every rounding step is skipped, which must give
+    plain attention (the rotation cancels in Q K^T).
+    Returns float64 ``(o, lse)``.
+    """
+    if mode not in ("block+had", "block", "tensor"):
+        raise ValueError(mode)
+    rot = signs if mode == "block+had" else None
+    per_tensor = mode == "tensor"
+    out = []
+    for x, sg in ((q, rot), (k, rot), (v, None)):
+        codes, s, y = quantize_fp8(x, signs=sg, per_tensor=per_tensor, quantize=quantize)
+        out.append(dequantize_fp8(codes, s) if quantize else y)
+    qh, kh, vh = out
+    return fp8_attention_emulate(qh, kh, vh, causal=causal, scale=scale, Bc=Bc, quantize_p=quantize)

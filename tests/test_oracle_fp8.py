@@ -1,0 +1,205 @@
+"""Pins for oracle/fp8.py: the E4M3 codec, the Hadamard rotation, block and
+per-tensor scales, and the FP8 attention emulation."""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+from oracle import (
+    E4M3_MAX,
+    attention_ref,
+    dequantize_fp8,
+    e4m3_decode,
+    e4m3_encode,
+    e4m3_round,
+    fp8_attention_emulate,
+    fp8_emulate,
+    hadamard_matrix,
+    quantize_fp8,
+    rotation_matrix,
+)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "e4m3_facts.txt")
+RNG = np.random.default_rng(99)
+
+
+def _golden_rows():
+    rows = []
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                c, v = line.split()
+                rows.append((int(c, 16), float(v)))
+    return rows
+
+
+def test_decode_golden_facts():
+    rows = _golden_rows()
+    assert (0x7E, E4M3_MAX) in rows
+    for c, v in rows:
+        got = e4m3_decode(np.uint8(c))
+        if math.isnan(v):
+            assert np.isnan(got)
+        else:
+            assert got == v and np.signbit(got) == np.signbit(v)
+
+
+def test_decode_matches_torch_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = e4m3_decode(codes)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[fin], ref[fin])
+    assert fin.sum() == 254
+    pos = got[:127]
+    assert np.all(np.diff(pos) > 0) and pos.max() == 448.0 and pos[1] == 2.0 ** -9
+
+
+def _torch_encode(x):
+    t = torch.from_numpy(np.clip(x, -E4M3_MAX, E4M3_MAX)).to(torch.float32)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_encode_matches_torch_dense_sweep_and_ties():
+    vals = e4m3_decode(np.arange(127, dtype=np.uint8))
+    mids = (vals[1:] + vals[:-1]) / 2  # exact ties (representable in float32)
+    eps = np.concatenate([mids * (1 - 2.0 ** -20), mids * (1 + 2.0 ** -20)])
+    grid = np.linspace(-460, 460, 200001)
+    small = np.linspace(-0.02, 0.02, 40001)
+    x = np.concatenate([vals, -vals, mids, -mids, eps, -eps, grid, small]).astype(np.float32).astype(np.float64)
+    got = e4m3_encode(x)
+    ref = _torch_encode(x)
+    # compare values (+0 and -0 are the same number)
+    np.testing.assert_array_equal(e4m3_decode(got), e4m3_decode(ref))
+
+
+def test_encode_decode_round_trip_and_saturation():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    np.testing.assert_array_equal(e4m3_encode(e4m3_decode(codes)), codes)
+    assert e4m3_round(1e6) == 448.0 and e4m3_round(-1e6) == -448.0
+    assert e4m3_round(2.0 ** -11) == 0.0  # below half the smallest subnormal
+    assert e4m3_round(1.0625) == 1.0  # tie between 1.0 and 1.125 goes to even
+    assert e4m3_round(1.1875) == 1.25  # tie between 1.125 and 1.25 goes to even
+    assert np.isnan(e4m3_round(np.nan))
+
+
+def test_rounding_error_bound():
+    x = RNG.standard_normal(100000) * 50
+    x = np.clip(x, -448, 448)
+    err = np.abs(e4m3_round(x) - x)
+    normal = np.abs(x) >= 2.0 ** -6
+    assert np.all(err[normal] <= np.abs(x[normal]) * 2.0 ** -4 + 1e-300)
+    assert np.all(err[~normal] <= 2.0 ** -10)
+
+
+@pytest.mark.parametrize("d", [1, 2, 4, 8, 16, 32, 64, 128, 256])
+def test_hadamard_is_sylvester_and_orthogonal(d):
+    Hm = hadamard_matrix(d)
+    np.testing.assert_array_equal(Hm, scipy.linalg.hadamard(d))
+    np.testing.assert_array_equal(Hm @ Hm.T, d * np.eye(d, dtype=np.int64))
+    s = RNG.choice([-1, 1], d)
+    M = rotation_matrix(s)
+    np.testing.assert_allclose(M @ M.T, np.eye(d), atol=1e-15)
+
+
+def test_rotation_preserves_scores_and_attention():
+    B, H, N, d = 1, 3, 50, 64
+    q, k, v = (RNG.standard_normal((B, H, N, d)) for _ in range(3))
+    signs = RNG.choice([-1, 1], (H, d))
+    _, _, qr = quantize_fp8(q, signs=signs, quantize=False)
+    _, _, kr = quantize_fp8(k, signs=signs, quantize=False)
+    for h in range(H):
+        np.testing.assert_allclose(qr[0, h] @ kr[0, h].T, q[0, h] @ k[0, h].T, atol=1e-12)
+    # the rotation is not the identity: coordinates really change
+    assert np.abs(qr - q).max() > 0.1
+    o1, l1 = attention_ref(q, k, v)
+    o2, l2 = attention_ref(qr, kr, v)
+    np.testing.assert_allclose(o1, o2, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, atol=1e-12)
+
+
+def test_rotation_spreads_a_channel_outlier():
+    d = 128
+    x = np.zeros((1, 1, 1, d))
+    x[0, 0, 0, 5] = 100.0
+    signs = RNG.choice([-1, 1], (1, d))
+    _, _, y = quantize_fp8(x, signs=signs, quantize=False)
+    np.testing.assert_allclose(np.abs(y), 100.0 / math.sqrt(d), atol=1e-12)
+
+
+@pytest.mark.parametrize("per_tensor", [False, True])
+def test_block_scales_invariants(per_tensor):
+    B, H, N, d = 2, 2, 300, 128
+    x = RNG.standard_normal((B, H, N, d))
+    x[0, 1, 130:140] *= 40  # an outlier region inside block 1
+    x[1, 0, 256:] = 0.0  # an all-zero (partial) last block
+    signs = None if per_tensor else RNG.choice([-1, 1], (H, d))
+    codes, s, y = quantize_fp8(x, signs=signs, per_tensor=per_tensor)
+    assert s.shape == (B, H, 3)
+    vals = np.abs(e4m3_decode(codes))
+    if per_tensor:
+        assert np.all(s == s.flat[0]) and vals.max() == 448.0
+        np.testing.assert_allclose(s.flat[0], np.abs(x).max() / 448.0, rtol=1e-15)
+    else:
+        for b in range(B):
+            for h in range(H):
+                for i in range(3):
+                    blk = vals[b, h, i * 128:(i + 1) * 128]
+                    if np.abs(y[b, h, i * 128:(i + 1) * 128]).max() == 0:
+                        assert s[b, h, i] == 1.0 and blk.max() == 0
+                    else:
+                        assert blk.max() == 448.0
+                        np.testing.assert_allclose(s[b, h, i], np.abs(y[b, h, i * 128:(i + 1) * 128]).max() / 448,
+                                                   rtol=1e-15)
+    # dequantised values are within half an E4M3 step of y (relative 2^-4)
+    xh = dequantize_fp8(codes, s)
+    srow = np.repeat(s, 128, axis=2)[:, :, :N, None]
+    assert np.all(np.abs(xh - y) <= np.maximum(np.abs(y) * 2.0 ** -4, srow * 2.0 ** -10) + 1e-12)
+
+
+@pytest.mark.parametrize("mode", ["block+had", "block", "tensor"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_emulate_without_rounding_is_attention(mode, causal):
+    B, H, N, d = 1, 2, 200, 64
+    q, k, v = (RNG.standard_normal((B, H, N, d)) for _ in range(3))
+    signs = RNG.choice([-1, 1], (H, d))
+    o, l = fp8_emulate(q, k, v, signs=signs, mode=mode, causal=causal, Bc=64, quantize=False)
+    o_ref, l_ref = attention_ref(q, k, v, causal=causal)
+    np.testing.assert_allclose(o, o_ref, atol=1e-12)
+    np.testing.assert_allclose(l, l_ref, atol=1e-12)
+
+
+def test_fp8_attention_emulate_matches_definition_on_dequantised_operands():
+    B, H, N, d = 1, 1, 150, 32
+    q, k, v = (RNG.standard_normal((B, H, N, d)) for _ in range(3))
+    qh, kh, vh = (dequantize_fp8(*quantize_fp8(x)[:2]) for x in (q, k, v))
+    o, l = fp8_attention_emulate(qh, kh, vh, Bc=64, quantize_p=False)
+    o_ref, l_ref = attention_ref(qh, kh, vh)
+    np.testing.assert_allclose(o, o_ref, atol=1e-12)
+    np.testing.assert_allclose(l, l_ref, atol=1e-12)
+
+
+def test_fp8_error_is_small_and_ordered_on_outliers():
+    # the rounded emulation stays close to exact attention, and per-block
+    # scaling with rotation does no worse than one scale per tensor on
+    # inputs with large outliers
+    B, H, N, d = 1, 2, 512, 128
+    g = np.random.default_rng(5)
+    q, k, v = (g.standard_normal((B, H, N, d)) for _ in range(3))
+    for x in (q, k, v):
+        m = g.random(x.shape) < 1e-3
+        x[m] = 10 * g.standard_normal(m.sum())
+    signs = g.choice([-1, 1], (H, d))
+    o_ref, _ = attention_ref(q, k, v)
+    rms = {}
+    for mode in ("block+had", "block", "tensor"):
+        o, _ = fp8_emulate(q, k, v, signs=signs, mode=mode, Bc=64)
+        rms[mode] = float(np.sqrt(np.mean((o - o_ref) ** 2)))
+    assert rms["block+had"] < 3e-2
+    assert rms["block+had"] <= rms["tensor"]
