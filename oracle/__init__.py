@@ -25,8 +25,8 @@ Modules:
 
 Every function is pinned by ``-m "not gpu"`` tests against facts that do not
 come from the oracle itself (brute force, closed forms, library routines,
-invariants).  The one reading that nothing on the pages fixes -- the 2^8
-pre-scale of probabilities before their E4M3 cast in the FP8 PV product -- is
+invariants).  The one reading that nothing on the pages fixes -- how
+probabilities are scaled before their E4M3 cast in the FP8 PV product -- is
 marked "parity unpinned" in :mod:`oracle.fp8`.
 """
 
@@ -42,4 +42,5 @@ from .fp8 import (  # noqa: F401
     dequantize_fp8,
     fp8_attention_emulate,
     fp8_emulate,
+    scale_mantissa,
 )

@@ -25,13 +25,17 @@ What the pages fix, and the readings taken where they are silent:
   "为什么 V 不使用同样的 Q/K 成对抵消").
 * FP8 attention: S = scale * Q^ K^T on the dequantised operands; both GEMM
   operands are FP8 while the softmax state stays fp32/fp64 (P1 section
-  "FP8 Attention 仍然不等于 FP8 全链路").  The probabilities that enter the PV
-  product are quantised as E4M3(P * 2^8) * 2^-8 with P = exp(S - m) in (0, 1];
-  the row sum l is taken from the unquantised P.  PARITY UNPINNED: the pages
-  never say how P is brought into FP8; the 2^8 pre-scale (exact, keeps P <=
-  256 < 448 and moves small probabilities out of the subnormal range) is this
-  build's reading.  It is pinned only in the sense that with quantisation
-  switched off the emulation equals :func:`oracle.attention.attention_ref`.
+  "FP8 Attention 仍然不等于 FP8 全链路"); the V block scale is applied at the
+  PV product (P1 section "Block Quantization 为什么优于 Per-Tensor Scale").
+  PARITY UNPINNED: the pages never say how the probabilities P = exp(S - m)
+  in (0, 1] are brought into FP8.  The reading taken here: write the V
+  block's scale as s_V = mu * 2^e with mu in [1, 2); P is quantised as
+  P_q = E4M3(P * 2^7 * mu) / (2^7 * mu), so that P * 2^7 * mu < 256 < 448
+  never saturates, small probabilities stay out of the subnormal range, and
+  the remaining factor 2^e * 2^-7 is an exact power of two.  The row sum l
+  is taken from the unquantised P.  The reading is pinned only in the sense
+  that with quantisation switched off the emulation equals
+  :func:`oracle.attention.attention_ref`.
 """
 
 from __future__ import annotations
@@ -51,11 +55,12 @@ __all__ = [
     "dequantize_fp8",
     "fp8_attention_emulate",
     "fp8_emulate",
+    "scale_mantissa",
 ]
 
 E4M3_MAX = 448.0  # P2 section 三.3
 SCALE_BLOCK = 128  # rows per scale block
-P_PRESCALE = 256.0  # 2^8, see module docstring (parity unpinned)
+P_PRESCALE_EXP = 7  # P is scaled by 2^7 * mantissa(s_V) before rounding (parity unpinned)
 
 
 def e4m3_decode(codes) -> np.ndarray:
@@ -161,19 +166,32 @@ def dequantize_fp8(codes, scale, block: int = SCALE_BLOCK) -> np.ndarray:
     return e4m3_decode(codes) * s_rows
 
 
-def fp8_attention_emulate(qh, kh, vh, causal: bool = False, scale=None, Bc: int = 64, quantize_p: bool = True):
+def scale_mantissa(s) -> np.ndarray:
+    """mu in [1, 2) with s = mu * 2^e for positive normal s."""
+    m, _ = np.frexp(np.asarray(s, dtype=np.float64))
+    return 2.0 * m
+
+
+def fp8_attention_emulate(qh, kh, vh, causal: bool = False, scale=None, Bc: int = 64, quantize_p: bool = True,
+                          v_scale=None, block: int = SCALE_BLOCK):
     """Online-softmax attention on already dequantised FP8 operands.
 
     ``qh, kh, vh`` are float64 ``[B, H, N, d]`` holding exactly the values the
     FP8 codes times their scales represent.  The recurrence is the one of
     :func:`oracle.attention.online_ref` with key blocks of ``Bc`` rows (the
     block size matters here: it decides the running max each probability is
-    quantised against).  With ``quantize_p`` the PV product uses
-    E4M3(P * 2^8) * 2^-8 while ``l`` sums the unquantised P.
+    quantised against; ``Bc`` must divide the scale block).  With
+    ``quantize_p`` the PV product uses P_q = E4M3(P * f) / f with
+    f = 2^7 * mantissa(s_V) of the key's V scale block (``v_scale``
+    ``[B, H, ceil(N / block)]``), while ``l`` sums the unquantised P.
     """
     qh, kh, vh = to_f64(qh), to_f64(kh), to_f64(vh)
     B, H, N, d = qh.shape
     Nk = kh.shape[2]
+    if quantize_p:
+        if v_scale is None or block % Bc:
+            raise ValueError("quantize_p needs v_scale and Bc dividing the scale block")
+        fq = np.exp2(P_PRESCALE_EXP) * scale_mantissa(v_scale)  # [B, H, nb]
     sc = scale_f64(scale, d)
     qi = np.arange(N)
     o = np.empty((B, H, N, vh.shape[3]))
@@ -194,7 +212,11 @@ def fp8_attention_emulate(qh, kh, vh, causal: bool = False, scale=None, Bc: int 
                 alpha = np.where(dead, 1.0, np.exp(m - safe))
                 P = np.where(dead[:, None], 0.0, np.exp(S - safe[:, None]))
                 l = alpha * l + P.sum(axis=1)
-                Pq = e4m3_round(P * P_PRESCALE) / P_PRESCALE if quantize_p else P
+                if quantize_p:
+                    f = fq[b, h, j0 // block]
+                    Pq = e4m3_round(P * f) / f
+                else:
+                    Pq = P
                 acc = alpha[:, None] * acc + Pq @ vh[b, h, j0:j1]
                 m = m_new
             o[b, h] = acc / l[:, None]
@@ -222,6 +244,6 @@ def fp8_emulate(q, k, v, signs=None, mode: str = "block+had", causal: bool = Fal
     out = []
     for x, sg in ((q, rot), (k, rot), (v, None)):
         codes, s, y = quantize_fp8(x, signs=sg, per_tensor=per_tensor, quantize=quantize)
-        out.append(dequantize_fp8(codes, s) if quantize else y)
-    qh, kh, vh = out
-    return fp8_attention_emulate(qh, kh, vh, causal=causal, scale=scale, Bc=Bc, quantize_p=quantize)
+        out.append((dequantize_fp8(codes, s) if quantize else y, s))
+    (qh, _), (kh, _), (vh, vs) = out
+    return fp8_attention_emulate(qh, kh, vh, causal=causal, scale=scale, Bc=Bc, quantize_p=quantize, v_scale=vs)

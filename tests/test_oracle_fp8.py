@@ -203,3 +203,21 @@ def test_fp8_error_is_small_and_ordered_on_outliers():
         rms[mode] = float(np.sqrt(np.mean((o - o_ref) ** 2)))
     assert rms["block+had"] < 3e-2
     assert rms["block+had"] <= rms["tensor"]
+
+
+def test_scale_mantissa_closed_form():
+    from oracle import scale_mantissa
+
+    s = np.array([1.0, 3.0, 0.75, 448.0, 2.0 ** -20 * 1.25, 1 / 448])
+    mu = scale_mantissa(s)
+    np.testing.assert_array_equal(mu, [1.0, 1.5, 1.5, 1.75, 1.25, 2 * 256 / 448])
+    e = np.log2(s / mu)
+    np.testing.assert_array_equal(e, np.round(e))  # s / mu is an exact power of two
+
+
+def test_p_quantisation_never_saturates():
+    # P in (0, 1] times 2^7 * mu with mu < 2 stays below 256 < 448
+    from oracle import scale_mantissa
+
+    mu = scale_mantissa(np.nextafter(2.0, 0))
+    assert 2.0 ** 7 * mu < 256 and e4m3_round(2.0 ** 7 * mu) <= 256
