@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Forward-attention throughput on one MI355X.
+
+One step = the bf16 exact-attention forward on the standard block
+(B=4, H=16, N=2048, d=128, bf16 N(0, 1) inputs, scale 1/sqrt(d)), run once
+non-causal and once causal, inputs resident in HBM.  FLOPs are counted as
+4 B H N^2 d per forward, halved for causal.  The JSON line also carries:
+
+* ``roofline`` of the dominant kernel (the non-causal bf16 forward), whose
+  average launch duration is measured with HIP events on the stream the
+  kernel runs on, against the dense bf16 MFMA peak (2516.6 TFLOP/s);
+* ``legs``: per-kernel figures -- the d=128 sequence-length sweep at 16384
+  total tokens (TFLOPS vs N, both causal flags), the FP8 workload
+  (B4 H16 N4096 d128) prep GB/s and FP8 forward TFLOPS against the FP8 peak;
+* ``cpu_baseline``: the CPU fp64 oracle timed on a bounded sample of the
+  same step on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_BF16 = 2516.6  # TFLOP/s, dense bf16 MFMA, MI355X public spec
+PEAK_FP8 = 5033.2
+PEAK_HBM = 8000.0  # GB/s
+METRIC = "attention fwd TFLOPS (bf16, fp8) at d=128 vs N, and % of MFMA peak"
+GPU_HOLD_CYCLES = 20_000_000  # a short device-side spin before each timed region
+
+
+def fwd_flops(B, H, N, d, causal):
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def _time_launches(fn, reps, warmup):
+    """Average duration (s) of fn() over reps, HIP events on the current stream."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(GPU_HOLD_CYCLES)  # lets the host queue every launch before the first event
+    ev[0].record()
+    for i in range(reps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ts = [ev[i].elapsed_time(ev[i + 1]) / 1e3 for i in range(reps)]
+    ts.sort()
+    return sum(ts) / len(ts), ts[len(ts) // 2]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="skip the sweep and FP8 legs (for profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (every (batch, head) pair is "
+              "independent, so more GPUs would each run this same kernel on their own share)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_attention_73_amd as fa
+    from exact_attention_73_amd.inputs import WORKLOADS, make_qkv, make_signs, softmax_scale, sweep_workloads
+
+    fa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WORKLOADS["std"]
+    B, H, N, d = w.B, w.H, w.N, w.d
+    q, k, v = (x.to(dev) for x in make_qkv(B, H, N, d, w.seed))
+    sc = softmax_scale(d)
+    o = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+    def step():
+        fa.fwd_bf16(q, k, v, causal=False, softmax_scale=sc, out=o, lse=lse)
+        fa.fwd_bf16(q, k, v, causal=True, softmax_scale=sc, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    # per-launch durations inside the timed region, on the kernels' stream
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    torch.cuda._sleep(GPU_HOLD_CYCLES)
+    ev[0].record()
+    for i in range(args.steps):
+        fa.fwd_bf16(q, k, v, causal=False, softmax_scale=sc, out=o, lse=lse)
+        ev[2 * i + 1].record()
+        fa.fwd_bf16(q, k, v, causal=True, softmax_scale=sc, out=o, lse=lse)
+        ev[2 * i + 2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    nc = [ev[2 * i].elapsed_time(ev[2 * i + 1]) / 1e3 for i in range(args.steps)]
+    ca = [ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) / 1e3 for i in range(args.steps)]
+    gpu_total = ev[0].elapsed_time(ev[-1]) / 1e3
+    step_flops = fwd_flops(B, H, N, d, False) + fwd_flops(B, H, N, d, True)
+    ms_per_step = 1e3 * gpu_total / args.steps
+    value = step_flops / (gpu_total / args.steps) / 1e12
+    t_nc = sum(nc) / len(nc)
+    t_ca = sum(ca) / len(ca)
+    achieved = fwd_flops(B, H, N, d, False) / t_nc / 1e12
+
+    legs = {
+        "bf16_std_noncausal_tflops": round(achieved, 2),
+        "bf16_std_causal_tflops": round(fwd_flops(B, H, N, d, True) / t_ca / 1e12, 2),
+        "bf16_std_noncausal_us": round(t_nc * 1e6, 2),
+        "bf16_std_causal_us": round(t_ca * 1e6, 2),
+    }
+    del q, k, v
+
+    if not args.quick:
+        sweep = {}
+        for sw in sweep_workloads():
+            if sw.d != 128:
+                continue
+            qs, ks, vs = (x.to(dev) for x in make_qkv(sw.B, sw.H, sw.N, sw.d, sw.seed))
+            row = {}
+            for causal in (False, True):
+                t, _ = _time_launches(lambda: fa.fwd_bf16(qs, ks, vs, causal=causal), 20, 3)
+                row["causal" if causal else "noncausal"] = round(fwd_flops(sw.B, sw.H, sw.N, sw.d, causal) / t / 1e12, 1)
+            sweep[str(sw.N)] = row
+            del qs, ks, vs
+        legs["bf16_d128_sweep_tflops"] = sweep
+
+        w8 = WORKLOADS["fp8"]
+        q, k, v = (x.to(dev) for x in make_qkv(w8.B, w8.H, w8.N, w8.d, w8.seed, outliers=True))
+        signs = make_signs(w8.H, w8.d, w8.seed + 1).to(dev)
+        q8, qs_ = fa.fp8_prep(q, signs=signs)
+        k8, ks_ = fa.fp8_prep(k, signs=signs)
+        v8t, vs_ = fa.fp8_prep(v, transpose=True)
+        t_prep, _ = _time_launches(lambda: fa.fp8_prep(q, signs=signs), 20, 3)
+        t_prep_v, _ = _time_launches(lambda: fa.fp8_prep(v, transpose=True), 20, 3)
+        t8, _ = _time_launches(lambda: fa.fwd_fp8(q8, k8, v8t, qs_, ks_, vs_), 20, 3)
+        elems = w8.B * w8.H * w8.N * w8.d
+        prep_bytes = elems * 2 + elems + w8.B * w8.H * ((w8.N + 127) // 128) * 4
+        f8 = fwd_flops(w8.B, w8.H, w8.N, w8.d, False)
+        tb, _ = _time_launches(lambda: fa.fwd_bf16(q, k, v), 20, 3)
+        legs["fp8"] = {
+            "workload": "B4 H16 N4096 d128 non-causal, 0.1% N(0,10^2) outliers",
+            "fwd_fp8_tflops": round(f8 / t8 / 1e12, 1),
+            "fwd_fp8_frac_of_fp8_peak": round(f8 / t8 / 1e12 / PEAK_FP8, 4),
+            "fwd_bf16_same_shape_tflops": round(f8 / tb / 1e12, 1),
+            "prep_qk_rotated_gbps": round(prep_bytes / t_prep / 1e9, 1),
+            "prep_v_transposed_gbps": round(prep_bytes / t_prep_v / 1e9, 1),
+            "end_to_end_tflops": round(f8 / (t8 + 2 * t_prep + t_prep_v) / 1e12, 1),
+        }
+        del q, k, v, q8, k8, v8t
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(B, H, N, d, w.seed)
+
+    props = torch.cuda.get_device_properties(0)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "standard block B4 H16 N2048 d128, bf16 forward, non-causal + causal per step",
+            "B": B, "H": H, "N": N, "d": d, "causal": [False, True],
+            "flop_convention": "4*B*H*N^2*d per forward, halved for causal",
+            "device": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count,
+            "host_wall_s": round(wall, 4),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "fwd_bf16_kernel<128, non-causal>",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16, 4),
+            "traffic": None,
+        },
+        "legs": legs,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(B, H, N, d, seed):
+    """The oracle, as it stands, on a bounded sample of heads of the step."""
+    import numpy as np
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = os.cpu_count() or 1
+    from exact_attention_73_amd.inputs import make_qkv, softmax_scale
+    from oracle import attention_ref
+
+    q, k, v = make_qkv(B, H, N, d, seed)
+    sc = softmax_scale(d)
+    qn, kn, vn = (x.float().numpy().astype(np.float64) for x in (q, k, v))
+
+    def run(nh):
+        t0 = time.perf_counter()
+        for causal in (False, True):
+            attention_ref(qn[:1, :nh], kn[:1, :nh], vn[:1, :nh], causal=causal, scale=sc)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    nh = int(max(1, min(H, 15.0 // max(t1, 1e-3))))
+    t = run(nh) if nh > 1 else t1
+    flops = fwd_flops(1, nh, N, d, False) + fwd_flops(1, nh, N, d, True)
+    return {
+        "value": round(flops / t / 1e12, 6),
+        "unit": "TFLOPS",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{nh} of {B * H} heads of the step (batch 0), non-causal + causal, fp64 NumPy, "
+                  f"{t:.2f} s; the oracle evaluates full score rows, so causal does twice the counted work",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,10 @@
+"""MI355X (gfx950) fused exact attention forward: bf16 and FP8 E4M3 paths.
+
+The compute lives in hand-written HIP kernels behind the C ABI of
+``include/fa.h`` (built into ``libfa.so`` next to this file); the functions
+here only marshal torch tensors into that ABI.
+"""
+
+from ._lib import FaError, fp8_prep, fp8_vt_ld, fwd_bf16, fwd_fp8, load  # noqa: F401
+
+__all__ = ["fwd_bf16", "fp8_prep", "fwd_fp8", "fp8_vt_ld", "load", "FaError"]

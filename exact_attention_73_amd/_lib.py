@@ -1,0 +1,144 @@
+"""ctypes binding of the C ABI in include/fa.h (argument marshalling only).
+
+Every step of the attention path runs in the HIP kernels of ``libfa.so``;
+this module only checks tensor metadata, allocates outputs with torch,
+passes raw device pointers and the current stream, and turns a non-zero
+status into an exception.  There is no other implementation to fall back
+to: if the library is missing or fails to load, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_NAME = "libfa.so"
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+FA_PREP_TRANSPOSE = 1
+FA_PREP_PER_TENSOR = 2
+
+# every function the header declares, with its ctypes signature
+_VP, _FP, _I, _F = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+SIGNATURES = {
+    "fa_fwd_bf16": (_I, [_VP, _VP, _VP, _FP, _FP, _I, _I, _I, _I, _I, _F, _VP]),
+    "fa_fp8_prep": (_I, [_VP, _VP, _FP, _VP, _I, _I, _I, _I, ctypes.c_uint, _VP]),
+    "fa_fp8_vt_ld": (_I, [_I]),
+    "fa_fwd_fp8": (_I, [_VP, _VP, _VP, _FP, _FP, _FP, _FP, _FP, _I, _I, _I, _I, _I, _F, _VP]),
+    "fa_status_string": (ctypes.c_char_p, [_I]),
+    "fa_abi_version": (_I, []),
+}
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the built library once; raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is not built; run __graft_entry__.build() (hipcc for gfx950) first")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise FaError(fn, status, load().fa_status_string(status).decode())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype, name: str):
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor on a GPU")
+
+
+def fwd_bf16(q, k, v, causal: bool = False, softmax_scale: float | None = None, out=None, lse=None):
+    """O, lse = attention(q, k, v) for bf16 ``[B, H, N, d]`` CUDA tensors.
+
+    Returns fp32 ``o [B, H, N, d]`` and fp32 ``lse [B, H, N]`` (natural log).
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, n)
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one shape [B, H, N, d]")
+    B, H, N, d = q.shape
+    scale = (1.0 / d ** 0.5) if softmax_scale is None else float(softmax_scale)
+    o = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if out is None else out
+    ls = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(o, torch.float32, "out")
+    _need(ls, torch.float32, "lse")
+    st = load().fa_fwd_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), ls.data_ptr(), B, H, N, d,
+                            int(bool(causal)), scale, _stream(q))
+    _check("fa_fwd_bf16", st)
+    return o, ls
+
+
+def fp8_vt_ld(N: int) -> int:
+    return int(load().fa_fp8_vt_ld(int(N)))
+
+
+def fp8_prep(x, signs=None, transpose: bool = False, per_tensor: bool = False):
+    """E4M3 codes and per-128-row scales of one bf16 ``[B, H, N, d]`` tensor.
+
+    ``signs``: int8 ``[H, d]`` of +-1 on the GPU (rotate, for Q and K) or None.
+    Returns ``(x8, scale)``: uint8 ``[B, H, N, d]`` (or ``[B, H, d, ld]`` when
+    ``transpose``) and fp32 ``[B, H, ceil(N / 128)]``.
+    """
+    _need(x, torch.bfloat16, "x")
+    B, H, N, d = x.shape
+    if signs is not None:
+        _need(signs, torch.int8, "signs")
+        if tuple(signs.shape) != (H, d):
+            raise ValueError("signs must be [H, d]")
+    nb = (N + 127) // 128
+    shape = (B, H, d, fp8_vt_ld(N)) if transpose else (B, H, N, d)
+    x8 = torch.empty(shape, dtype=torch.uint8, device=x.device)
+    sc = torch.empty((B, H, nb), dtype=torch.float32, device=x.device)
+    flags = (FA_PREP_TRANSPOSE if transpose else 0) | (FA_PREP_PER_TENSOR if per_tensor else 0)
+    st = load().fa_fp8_prep(x.data_ptr(), x8.data_ptr(), sc.data_ptr(), None if signs is None else signs.data_ptr(),
+                            B, H, N, d, flags, _stream(x))
+    _check("fa_fp8_prep", st)
+    return x8, sc
+
+
+def fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, causal: bool = False, softmax_scale: float | None = None,
+            out=None, lse=None):
+    """Attention forward on the FP8 operands made by :func:`fp8_prep`."""
+    for t, n in ((q8, "q8"), (k8, "k8"), (v8t, "v8t")):
+        _need(t, torch.uint8, n)
+    for t, n in ((q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+        _need(t, torch.float32, n)
+    B, H, N, d = q8.shape
+    if k8.shape != q8.shape or tuple(v8t.shape) != (B, H, d, fp8_vt_ld(N)):
+        raise ValueError("k8 must match q8 and v8t must be [B, H, d, fa_fp8_vt_ld(N)]")
+    nb = (N + 127) // 128
+    for t in (q_scale, k_scale, v_scale):
+        if tuple(t.shape) != (B, H, nb):
+            raise ValueError("scales must be [B, H, ceil(N / 128)]")
+    scale = (1.0 / d ** 0.5) if softmax_scale is None else float(softmax_scale)
+    o = torch.empty((B, H, N, d), dtype=torch.float32, device=q8.device) if out is None else out
+    ls = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if lse is None else lse
+    _need(o, torch.float32, "out")
+    _need(ls, torch.float32, "lse")
+    st = load().fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8t.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(),
+                           v_scale.data_ptr(), o.data_ptr(), ls.data_ptr(), B, H, N, d, int(bool(causal)), scale,
+                           _stream(q8))
+    _check("fa_fwd_fp8", st)
+    return o, ls

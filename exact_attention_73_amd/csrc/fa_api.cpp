@@ -1,0 +1,159 @@
+// C ABI of the library (declared in include/fa.h): argument validation,
+// the gfx950 device check, and dispatch to the kernel launchers.
+#include "fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "fa_kernels.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = something else
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return FA_ERR_DEVICE;
+  }
+  if (dev >= kMaxDevices) return FA_ERR_DEVICE;
+  int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return FA_ERR_DEVICE;
+    }
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? FA_OK : FA_ERR_DEVICE;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  const double elems = (double)B * (double)H * (double)N * (double)d;
+  if (elems >= 1099511627776.0) return FA_ERR_SHAPE;  // 2^40
+  // the grid is B * H * ceil(N / 128) workgroups
+  if ((double)B * (double)H * (double)((N + 127) / 128) >= 2147483647.0) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int check_scale(float s) { return (std::isfinite(s) && s > 0.f) ? FA_OK : FA_ERR_ARG; }
+
+int launch_status(hipError_t e) {
+  if (e == hipSuccess) return FA_OK;
+  (void)hipGetLastError();
+  return FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL_PTR: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "B, H and N must be >= 1 and the tensors smaller than 2^40 elements";
+    case FA_ERR_HEADDIM: return "head dimension not supported by this entry point";
+    case FA_ERR_ARG: return "invalid argument (causal must be 0/1, softmax_scale finite and > 0, known flags)";
+    case FA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case FA_ERR_DEVICE: return "no HIP device, or the current device is not gfx950";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int fa_fp8_vt_ld(int N) { return N < 1 ? 0 : ((N + 127) / 128) * 128; }
+
+int fa_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int N, int d,
+                int causal, float softmax_scale, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_PTR;
+  if (int e = check_shape(B, H, N, d == 64 || d == 128 || d == 256 ? d : 1)) return e;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_HEADDIM;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (int e = check_scale(softmax_scale)) return e;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  if (int e = check_device()) return e;
+
+  fa::FwdBf16Params p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.scale = softmax_scale;
+  p.c = softmax_scale * 1.4426950408889634f;
+  return launch_status(fa::launch_fwd_bf16(p, d, causal == 1, static_cast<hipStream_t>(stream)));
+}
+
+int fa_fp8_prep(const void* x, void* x8, float* x_scale, const signed char* signs, int B, int H, int N, int d,
+                unsigned flags, void* stream) {
+  if (!x || !x8 || !x_scale) return FA_ERR_NULL_PTR;
+  if (int e = check_shape(B, H, N, d == 128 ? d : 1)) return e;
+  if (d != 128) return FA_ERR_HEADDIM;
+  if (flags & ~(FA_PREP_TRANSPOSE | FA_PREP_PER_TENSOR)) return FA_ERR_ARG;
+  if (!aligned16(x) || !aligned16(x8) || !aligned16(x_scale)) return FA_ERR_ALIGN;
+  if (int e = check_device()) return e;
+
+  fa::Fp8PrepParams p;
+  p.x = static_cast<const uint16_t*>(x);
+  p.x8 = static_cast<uint8_t*>(x8);
+  p.scale = x_scale;
+  p.signs = reinterpret_cast<const int8_t*>(signs);
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.ld = fa_fp8_vt_ld(N);
+  p.transpose = (flags & FA_PREP_TRANSPOSE) != 0;
+  p.per_tensor = (flags & FA_PREP_PER_TENSOR) != 0;
+  return launch_status(fa::launch_fp8_prep(p, d, static_cast<hipStream_t>(stream)));
+}
+
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* q_scale, const float* k_scale,
+               const float* v_scale, float* o, float* lse, int B, int H, int N, int d, int causal,
+               float softmax_scale, void* stream) {
+  if (!q8 || !k8 || !v8t || !q_scale || !k_scale || !v_scale || !o || !lse) return FA_ERR_NULL_PTR;
+  if (int e = check_shape(B, H, N, d == 128 ? d : 1)) return e;
+  if (d != 128) return FA_ERR_HEADDIM;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (int e = check_scale(softmax_scale)) return e;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8t) || !aligned16(q_scale) || !aligned16(k_scale) ||
+      !aligned16(v_scale) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  if (int e = check_device()) return e;
+
+  fa::FwdFp8Params p;
+  p.q8 = static_cast<const uint8_t*>(q8);
+  p.k8 = static_cast<const uint8_t*>(k8);
+  p.v8t = static_cast<const uint8_t*>(v8t);
+  p.qs = q_scale;
+  p.ks = k_scale;
+  p.vs = v_scale;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.ld = fa_fp8_vt_ld(N);
+  p.scale = softmax_scale;
+  p.c = softmax_scale * 1.4426950408889634f;
+  return launch_status(fa::launch_fwd_fp8(p, d, causal == 1, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

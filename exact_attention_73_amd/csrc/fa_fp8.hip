@@ -1,0 +1,422 @@
+// FP8 E4M3 path for gfx950: the prep kernel (rotation, block scales,
+// quantisation, V transpose) and the FP8 attention forward.
+//
+// Prep (FA3 explainer "FlashAttention-3：用异步流水榨出 Hopper 的 Attention 性能",
+// sections "Block Quantization 为什么优于 Per-Tensor Scale" and "Incoherent
+// Processing 如何摊平离群值"; E4M3 largest value 448 from the wmrh.cn
+// FlashAttention V3 article, section 三.3):
+//   y = x diag(sigma_h) H_d (unnormalised fast Walsh-Hadamard transform,
+//       log2(d) butterfly stages: 3 inside a lane, 4 across 16 lanes),
+//   a = max |y| over each 128-row block, codes = RNE(y * 448 / a),
+//   stored scale s = a / (448 sqrt(d)) for rotated tensors (the 1/sqrt(d)
+//   of the orthonormal rotation is folded into s), a / 448 otherwise.
+// One workgroup per (batch, head, 128-row block); HBM-bound: it reads the
+// bf16 tensor once and writes the codes once.  V is written transposed,
+// [d][ld], through an LDS transpose, so the forward kernel's PV operand is
+// key-contiguous ("FP8 路径的第一个问题：WGMMA Layout" section: the transpose is
+// fused into a pass that happens anyway instead of costing its own HBM
+// round trip).
+//
+// Forward: same decomposition and online softmax as the bf16 kernel (one
+// workgroup of 4 waves per 128 query rows, S^T = K Q^T and O^T = V^T P^T on
+// v_mfma_f32_32x32x64_f8f6f4, fp32 accumulation and softmax state).  Scores
+// are descaled by folding s_Q,i * s_K,j into the exp2 constant of each
+// tile; probabilities are produced directly as P * 2^7 * mu_j (exp2 bias)
+// and cast to E4M3, and the PV instruction's block exponents supply
+// 2^-7 (P) and 2^e_j (V), where s_V,j = mu_j * 2^e_j.
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+namespace {
+
+constexpr float kE4M3Max = 448.f;
+
+// ---------------------------------------------------------------------------
+// prep
+// ---------------------------------------------------------------------------
+enum PrepMode { kPrepFused = 0, kPrepAmaxOnly = 1, kPrepGlobalScale = 2 };
+
+__device__ __forceinline__ uint32_t cvt_e4m3x4(float a, float b, float c, float d) {
+  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+__device__ __forceinline__ float clamp_e4m3(float x) { return __builtin_fminf(__builtin_fmaxf(x, -kE4M3Max), kE4M3Max); }
+
+// One workgroup = 256 threads = 16 row groups x 16 lanes; a lane owns 8
+// consecutive d of 8 consecutive rows (row = 8 * group + it).
+template <int MODE>
+__global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8PrepParams p) {
+  constexpr int D = 128;
+  __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t tr[D][128 + 16];  // transposed codes, padded rows
+
+  const int nb = (p.N + 127) / 128;
+  const int blk = blockIdx.x % nb;
+  const int bh = blockIdx.x / nb;
+  const int h = bh % p.H;
+  const int tid = threadIdx.x, lr = tid & 15, grp = tid >> 4;
+  const int n0 = blk * 128;
+  const uint16_t* X = p.x + (size_t)bh * p.N * D;
+  const bool rot = p.signs != nullptr;
+
+  float sg[8];
+  if (rot) {
+    const int8_t* s8 = p.signs + h * D + lr * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sg[e] = (float)s8[e];
+  }
+
+  float y[8][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int n = n0 + grp * 8 + it;
+    u32x4 raw = n < p.N ? *reinterpret_cast<const u32x4*>(X + (size_t)n * D + lr * 8) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y[it][2 * e] = __uint_as_float(raw[e] << 16);
+      y[it][2 * e + 1] = __uint_as_float(raw[e] & 0xffff0000u);
+    }
+    if (rot) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[it][e] *= sg[e];
+      // butterflies over index bits 0..2 (inside the lane)
+#pragma unroll
+      for (int b = 1; b < 8; b <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (!(e & b)) {
+            const float u = y[it][e], w = y[it][e + b];
+            y[it][e] = u + w;
+            y[it][e + b] = u - w;
+          }
+      // butterflies over index bits 3..6 (lanes lr ^ 1, 2, 4, 8 of the row)
+#pragma unroll
+      for (int b = 1; b < 16; b <<= 1) {
+        const bool upper = (lr & b) != 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float o = __shfl_xor(y[it][e], b, 16);
+          y[it][e] = upper ? (o - y[it][e]) : (y[it][e] + o);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(y[it][e]));
+  }
+
+  const float norm = rot ? 11.313708498984761f : 1.f;  // sqrt(128)
+  float inv;  // multiplier turning y into the E4M3 range
+  if (MODE == kPrepGlobalScale) {
+    inv = 1.f / (p.scale[0] * norm);
+  } else {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off, 64));
+    if ((tid & 63) == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+    if (MODE == kPrepAmaxOnly) {
+      if (tid == 0) p.scale[blockIdx.x] = amax;  // raw amax of y; turned into s by the reduce kernel
+      return;
+    }
+    if (tid == 0) p.scale[blockIdx.x] = amax > 0.f ? amax / (kE4M3Max * norm) : 1.f;
+    inv = amax > 0.f ? kE4M3Max / amax : 0.f;
+  }
+
+  if (!p.transpose) {
+    uint8_t* Y = p.x8 + (size_t)bh * p.N * D;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int n = n0 + grp * 8 + it;
+      u32x2 w;
+      w[0] = cvt_e4m3x4(clamp_e4m3(y[it][0] * inv), clamp_e4m3(y[it][1] * inv), clamp_e4m3(y[it][2] * inv),
+                        clamp_e4m3(y[it][3] * inv));
+      w[1] = cvt_e4m3x4(clamp_e4m3(y[it][4] * inv), clamp_e4m3(y[it][5] * inv), clamp_e4m3(y[it][6] * inv),
+                        clamp_e4m3(y[it][7] * inv));
+      if (n < p.N) *reinterpret_cast<u32x2*>(Y + (size_t)n * D + lr * 8) = w;
+    }
+  } else {
+    // codes of d = 8 lr + e, rows 8 grp .. 8 grp + 7 -> tr[d][8 grp .. +7]
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      u32x2 w;
+      w[0] = cvt_e4m3x4(clamp_e4m3(y[0][e] * inv), clamp_e4m3(y[1][e] * inv), clamp_e4m3(y[2][e] * inv),
+                        clamp_e4m3(y[3][e] * inv));
+      w[1] = cvt_e4m3x4(clamp_e4m3(y[4][e] * inv), clamp_e4m3(y[5][e] * inv), clamp_e4m3(y[6][e] * inv),
+                        clamp_e4m3(y[7][e] * inv));
+      *reinterpret_cast<u32x2*>(&tr[lr * 8 + e][grp * 8]) = w;
+    }
+    __syncthreads();
+    // row d of the block: 128 bytes = 8 x 16 B; 256 threads write 2 chunks each
+    uint8_t* Y = p.x8 + (size_t)bh * D * p.ld;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ci = tid + 256 * i, d = ci >> 3, ch = ci & 7;
+      *reinterpret_cast<u32x4*>(Y + (size_t)d * p.ld + n0 + ch * 16) = *reinterpret_cast<const u32x4*>(&tr[d][ch * 16]);
+    }
+  }
+}
+
+// Global amax over all block amaxes -> one scale written to every entry.
+__global__ __launch_bounds__(1024) void fp8_tensor_scale_kernel(float* scale, int n, float norm) {
+  __shared__ float red[16];
+  float a = 0.f;
+  for (int i = threadIdx.x; i < n; i += 1024) a = __builtin_fmaxf(a, scale[i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, off, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  __syncthreads();
+  a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a = __builtin_fmaxf(a, red[i]);
+  const float s = a > 0.f ? a / (kE4M3Max * norm) : 1.f;
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += 1024) scale[i] = s;
+}
+
+// ---------------------------------------------------------------------------
+// forward
+// ---------------------------------------------------------------------------
+constexpr int kWaves = 4;
+constexpr int kQW = 32;
+constexpr int kBR = kWaves * kQW;  // 128 = one scale block of queries
+constexpr int kBC = 64;            // keys per tile (half a scale block)
+constexpr int kThreads = 256;
+
+// 16-byte chunk swizzles (see the bf16 kernel): K rows are 128 bytes, V^T
+// tile rows are 64 bytes.
+__device__ __forceinline__ int k8_swizzle(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int v8_swizzle(int d) { return (d >> 2) & 3; }
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
+  constexpr int D = 128;
+  constexpr int NKB = kBC / 32;  // 2
+  constexpr int NDB = D / 32;    // 4
+  constexpr int NQS = D / 64;    // 2 k-steps of 64 d
+
+  __shared__ __attribute__((aligned(16))) uint8_t Ks[2][kBC * D];  // [key][d], swizzled
+  __shared__ __attribute__((aligned(16))) uint8_t Vs[2][D * kBC];  // [d][64 keys], permuted + swizzled
+
+  const int N = p.N;
+  const int BH = p.B * p.H;
+  const int nq = (N + kBR - 1) / kBR;
+  const int nb = nq;  // scale blocks per head (128 rows)
+  int bh, qt;
+  if constexpr (CAUSAL) {
+    qt = nq - 1 - (int)blockIdx.x / BH;
+    bh = (int)blockIdx.x % BH;
+  } else {
+    const int w = xcd_contiguous((int)blockIdx.x, (int)gridDim.x);
+    bh = w / nq;
+    qt = w % nq;
+  }
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const uint8_t* __restrict__ Qg = p.q8 + (size_t)bh * N * D;
+  const uint8_t* __restrict__ Kg = p.k8 + (size_t)bh * N * D;
+  const uint8_t* __restrict__ Vg = p.v8t + (size_t)bh * D * p.ld;
+  const float* __restrict__ ks = p.ks + (size_t)bh * nb;
+  const float* __restrict__ vs = p.vs + (size_t)bh * nb;
+  const int q0 = qt * kBR + wave * kQW;
+  const int qrow = q0 + l32;
+  const float cq = p.c * p.qs[(size_t)bh * nb + qt];
+
+  // Q^T operand: k-step s holds d = 64 s + 32 hi .. +31 of row qrow
+  i32x8 qreg[NQS];
+  {
+    const bool ok = qrow < N;
+    const u32x4* src = reinterpret_cast<const u32x4*>(Qg + (size_t)(ok ? qrow : 0) * D);
+#pragma unroll
+    for (int s = 0; s < NQS; ++s) {
+      const u32x4 a = ok ? src[4 * s + 2 * hi] : u32x4{0, 0, 0, 0};
+      const u32x4 b = ok ? src[4 * s + 2 * hi + 1] : u32x4{0, 0, 0, 0};
+      qreg[s] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+    }
+  }
+
+  const int kend = CAUSAL ? min(N, qt * kBR + kBR) : N;
+  const int ntiles = (kend + kBC - 1) / kBC;
+
+  // K tile: 64 rows x 8 chunks = 512 chunks, 2 per thread.
+  // V^T tile: 128 rows (d) x 64 keys = 2 halves of 32 bytes per row, one
+  // half per thread; dword i of the row moves to (i & 1) * 8 + (i >> 1).
+  u32x4 kpre[2];
+  u32x4 vpre[2];
+  auto load_tile = [&](int j) {
+    const int key0 = j * kBC;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ci = tid + kThreads * i, row = ci >> 3, ch = ci & 7, key = key0 + row;
+      kpre[i] = key < N ? *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + ch * 16) : u32x4{0, 0, 0, 0};
+    }
+    const int d = tid >> 1, half = tid & 1;
+    const u32x4* src = reinterpret_cast<const u32x4*>(Vg + (size_t)d * p.ld + key0 + half * 32);
+    vpre[0] = src[0];  // padded to a multiple of 128 columns: always in bounds
+    vpre[1] = src[1];
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ci = tid + kThreads * i, row = ci >> 3, ch = ci & 7;
+      *reinterpret_cast<u32x4*>(&Ks[buf][row * D + ((ch ^ k8_swizzle(row)) * 16)]) = kpre[i];
+    }
+    const int d = tid >> 1, half = tid & 1;
+    // dwords 16 half + {0, 2, 4, 6} -> slot half (chunk half), {1, 3, 5, 7} -> chunk 2 + half
+    const u32x4 ev = {vpre[0][0], vpre[0][2], vpre[1][0], vpre[1][2]};
+    const u32x4 od = {vpre[0][1], vpre[0][3], vpre[1][1], vpre[1][3]};
+    uint8_t* row = &Vs[buf][d * kBC];
+    *reinterpret_cast<u32x4*>(row + ((half ^ v8_swizzle(d)) * 16)) = ev;
+    *reinterpret_cast<u32x4*>(row + (((2 + half) ^ v8_swizzle(d)) * 16)) = od;
+  };
+
+  float m_run = -INFINITY;  // running max of the log2-domain scores of row qrow
+  float l_run = 0.f;
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < ntiles) load_tile(j + 1);
+    const int key0 = j * kBC;
+    const bool active = !CAUSAL || key0 <= q0 + kQW - 1;
+    if (active) {
+      const int sb = key0 >> 7;  // scale block of this key tile
+      const float ct = cq * ks[sb];
+      const float sv = vs[sb];
+      const uint32_t svb = __float_as_uint(sv);
+      const int v_exp = (int)((svb >> 23) & 0xffu);                   // E8M0 block exponent of s_V
+      const float mu = __uint_as_float((svb & 0x007fffffu) | 0x3f800000u);  // s_V mantissa in [1, 2)
+      const float pbias = 7.f + __builtin_amdgcn_logf(mu);           // log2(2^7 mu)
+      const float inv_f = 1.f / (128.f * mu);
+
+      f32x16 s[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        s[kb] = f32x16{};
+        const int row = kb * 32 + l32;
+        const uint8_t* krow = &Ks[buf][row * D];
+        const int sw = k8_swizzle(row);
+#pragma unroll
+        for (int st = 0; st < NQS; ++st) {
+          const u32x4 a0 = *reinterpret_cast<const u32x4*>(krow + (((4 * st + 2 * hi) ^ sw) * 16));
+          const u32x4 a1 = *reinterpret_cast<const u32x4*>(krow + (((4 * st + 2 * hi + 1) ^ sw) * 16));
+          const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2],
+                           (int)a1[3]};
+          s[kb] = mfma_fp8_32x32x64(a, qreg[st], s[kb], 127, 127);
+        }
+      }
+      const bool need_mask = (CAUSAL && key0 + kBC - 1 > q0) || (key0 + kBC > N);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const bool dead = (CAUSAL && key > qrow) || key >= N;
+            s[kb][r] = dead ? -INFINITY : s[kb][r];
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = fmax3(mx, s[kb][r], s[kb][r + 1]);
+      mx = __builtin_fmaxf(mx, swap_halves(mx)) * ct;  // ct > 0; -inf stays -inf
+      const float m_new = __builtin_fmaxf(m_run, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = exp2_fast(m_run - m_use);
+      const float moff = m_use - pbias;
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = exp2_fast(__builtin_fmaf(s[kb][r], ct, -moff));  // P * 2^7 * mu
+          s[kb][r] = e;
+          lsum += e;
+        }
+      l_run = alpha * l_run + lsum * inv_f;
+      m_run = m_new;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+      // P^T operand: byte 4w + t of the lane = register 4(w%4) + t of block w/4
+      i32x8 pb;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int kb = w >> 2, r = 4 * (w & 3);
+        pb[w] = (int)cvt_e4m3x4(s[kb][r], s[kb][r + 1], s[kb][r + 2], s[kb][r + 3]);
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int d = db * 32 + l32;
+        const uint8_t* vrow = &Vs[buf][d * kBC];
+        const int sw = v8_swizzle(d);
+        // slot order in the row: chunk 0 = even dwords of half 0, 1 = even of
+        // half 1, 2 = odd of half 0, 3 = odd of half 1; lane half hi needs the
+        // keys 8w + 4hi .. +3 (w = 0..7) = dword 2w + hi of the 64-key row,
+        // which are exactly chunks 2hi and 2hi + 1 in order.
+        const u32x4 c0 = *reinterpret_cast<const u32x4*>(vrow + (((2 * hi) ^ sw) * 16));
+        const u32x4 c1 = *reinterpret_cast<const u32x4*>(vrow + (((2 * hi + 1) ^ sw) * 16));
+        const i32x8 a = {(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], (int)c1[0], (int)c1[1], (int)c1[2],
+                         (int)c1[3]};
+        o[db] = mfma_fp8_32x32x64(a, pb, o[db], v_exp, 127 - 7);
+      }
+    }
+    if (j + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + swap_halves(l_run);
+  if (qrow < N) {
+    const float inv = 1.f / l_tot;
+    float* orow = p.o + (size_t)bh * N * D + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 val = {o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
+                           o[db][4 * g + 3] * inv};
+        *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * g + 4 * hi) = val;
+      }
+    if (hi == 0) p.lse[(size_t)bh * N + qrow] = m_run * 0.6931471805599453f + __logf(l_tot);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fp8_prep(const Fp8PrepParams& p, int d, hipStream_t stream) {
+  if (d != 128) return hipErrorInvalidValue;
+  const int nb = (p.N + 127) / 128;
+  const unsigned grid = (unsigned)nb * (unsigned)p.B * (unsigned)p.H;
+  if (!p.per_tensor) {
+    hipLaunchKernelGGL(fp8_prep_kernel<kPrepFused>, dim3(grid), dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(fp8_prep_kernel<kPrepAmaxOnly>, dim3(grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(fp8_tensor_scale_kernel, dim3(1), dim3(1024), 0, stream, p.scale, (int)grid,
+                     p.signs ? 11.313708498984761f : 1.f);
+  hipLaunchKernelGGL(fp8_prep_kernel<kPrepGlobalScale>, dim3(grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_fp8(const FwdFp8Params& p, int d, bool causal, hipStream_t stream) {
+  if (d != 128) return hipErrorInvalidValue;
+  const int nq = (p.N + kBR - 1) / kBR;
+  const unsigned grid = (unsigned)nq * (unsigned)p.B * (unsigned)p.H;
+  if (causal)
+    hipLaunchKernelGGL(fwd_fp8_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(fwd_fp8_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace fa

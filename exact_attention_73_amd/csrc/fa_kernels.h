@@ -1,0 +1,52 @@
+// Host-side launch entry points of the gfx950 kernels (internal to the
+// library; the public C ABI is include/fa.h).  Arguments have been validated
+// by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdBf16Params {
+  const uint16_t* q;  // bf16 [B, H, N, d]
+  const uint16_t* k;
+  const uint16_t* v;
+  float* o;    // fp32 [B, H, N, d]
+  float* lse;  // fp32 [B, H, N]
+  int B, H, N;
+  float scale;   // softmax scale
+  float c;       // scale * log2(e)
+};
+
+hipError_t launch_fwd_bf16(const FwdBf16Params& p, int d, bool causal, hipStream_t stream);
+
+struct Fp8PrepParams {
+  const uint16_t* x;   // bf16 [B, H, N, d]
+  uint8_t* x8;         // E4M3 codes, [B, H, N, d] or [B, H, d, ld]
+  float* scale;        // fp32 [B, H, nb]
+  const int8_t* signs; // [H, d] or nullptr
+  int B, H, N, ld;
+  bool transpose;
+  bool per_tensor;
+};
+
+hipError_t launch_fp8_prep(const Fp8PrepParams& p, int d, hipStream_t stream);
+
+struct FwdFp8Params {
+  const uint8_t* q8;  // [B, H, N, d]
+  const uint8_t* k8;  // [B, H, N, d]
+  const uint8_t* v8t; // [B, H, d, ld]
+  const float* qs;    // [B, H, nb]
+  const float* ks;
+  const float* vs;
+  float* o;
+  float* lse;
+  int B, H, N, ld;
+  float scale;
+  float c;
+};
+
+hipError_t launch_fwd_fp8(const FwdFp8Params& p, int d, bool causal, hipStream_t stream);
+
+}  // namespace fa

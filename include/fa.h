@@ -1,0 +1,142 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) fused exact attention forward library.
+ *
+ * The library computes O = softmax(scale * Q K^T) V and the row logsumexp,
+ * tile by tile with an online softmax, without ever writing the N x N score
+ * matrix to memory (wmrh.cn FlashAttention V3 article, sections 一.1 and
+ * 二.1; "FlashAttention-3：用异步流水榨出 Hopper 的 Attention 性能",
+ * section "Online Softmax 仍是精确合并的核心").  An FP8 E4M3 variant uses
+ * per-block scales and a random-sign Hadamard rotation of Q and K (same
+ * explainer, sections "Block Quantization 为什么优于 Per-Tensor Scale" and
+ * "Incoherent Processing 如何摊平离群值").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *   library allocates no memory and keeps no state besides a per-device
+ *   cache of the device's architecture check; it is safe to call from
+ *   several host threads.
+ * - Tensors are dense row-major ("contiguous").  Layout [B, H, N, d] means
+ *   element (b, h, n, i) sits at ((b * H + h) * N + n) * d + i.
+ * - Every pointer must be 16-byte aligned (FA_ERR_ALIGN otherwise).
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *   the call returns without waiting.  Faults inside a kernel surface at the
+ *   caller's next synchronisation.
+ * - Return value: FA_OK (0) or a negative FA_ERR_* code.  Arguments are
+ *   validated before any device work is issued; on an error nothing is
+ *   enqueued and no output is touched.  Nothing is printed and no C++
+ *   exception crosses the ABI.
+ * - There is no fallback: a case the kernels do not cover is an error,
+ *   never a slower path.  The kernels are built for gfx950 only; any other
+ *   device gives FA_ERR_DEVICE.
+ * - Causal masking: query row i attends to key j iff j <= i (queries and
+ *   keys have the same length N).
+ * - logsumexp is the natural log of sum_j exp(scale * q_i . k_j) over the
+ *   keys row i attends to, fp32 [B, H, N].
+ */
+#ifndef EXACT_ATTENTION_FA_H
+#define EXACT_ATTENTION_FA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL_PTR = -1, /* a required pointer is NULL                              */
+  FA_ERR_SHAPE = -2,    /* B, H or N < 1, or an element count >= 2^40              */
+  FA_ERR_HEADDIM = -3,  /* d not supported by this entry point                     */
+  FA_ERR_ARG = -4,      /* causal not 0/1, scale not finite and > 0, bad flags     */
+  FA_ERR_ALIGN = -5,    /* a pointer is not 16-byte aligned                        */
+  FA_ERR_DEVICE = -6,   /* no device, or the current device is not gfx950          */
+  FA_ERR_LAUNCH = -7    /* the kernel launch itself failed                         */
+};
+
+/* Flags of fa_fp8_prep. */
+#define FA_PREP_TRANSPOSE 1u  /* write x8 transposed, [B, H, d, fa_fp8_vt_ld(N)]       */
+#define FA_PREP_PER_TENSOR 2u /* one scale for the whole tensor (the comparison mode) */
+
+/*
+ * fa_fwd_bf16 -- exact attention forward, bf16 operands, fp32 accumulation.
+ *
+ *   q, k, v : bf16 [B, H, N, d]   (read only)
+ *   o       : fp32 [B, H, N, d]   (every element written)
+ *   lse     : fp32 [B, H, N]      (every element written, natural log)
+ *   d       : 64, 128 or 256      (FA_ERR_HEADDIM otherwise)
+ *   causal  : 0 or 1
+ *   softmax_scale : finite, > 0 (the usual value is 1/sqrt(d)).
+ *
+ * Any N >= 1 is accepted; tiles past N are masked.
+ */
+int fa_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int N, int d,
+                int causal, float softmax_scale, void* stream);
+
+/*
+ * fa_fp8_prep -- one pass over one tensor that produces the FP8 operands of
+ * fa_fwd_fp8 ("Incoherent Processing" and "Block Quantization" sections of
+ * the FA3 explainer cited above; E4M3 largest value 448 from the wmrh.cn
+ * article, section 三.3).
+ *
+ *   x       : bf16 [B, H, N, d]  (read only)
+ *   signs   : int8 [H, d] of +1/-1, or NULL.  When given, each row is
+ *             rotated, y = x diag(signs[h]) H_d / sqrt(d) with H_d the
+ *             Sylvester Hadamard matrix (apply the same signs to Q and K;
+ *             never to V).  NULL: y = x.
+ *   x8      : uint8 E4M3 (OCP e4m3fn) codes of y / s:
+ *             [B, H, N, d] by default, or with FA_PREP_TRANSPOSE the
+ *             transposed [B, H, d, ld] with ld = fa_fp8_vt_ld(N); columns
+ *             N..ld-1 are written as zero codes.
+ *   x_scale : fp32 [B, H, ceil(N / 128)]: s = amax(|y|) / 448 over each block
+ *             of 128 rows (all of d); s = 1 for an all-zero block.  With
+ *             FA_PREP_PER_TENSOR, amax runs over the whole tensor and every
+ *             entry holds the same s.
+ *   d       : 128.
+ *   flags   : OR of FA_PREP_TRANSPOSE and FA_PREP_PER_TENSOR (FA_ERR_ARG for
+ *             any other bit).
+ *
+ * Codes are round-to-nearest-even of clamp(y * 448 / amax, -448, 448).
+ * Per-tensor mode issues three kernels on `stream` (block amax, global
+ * amax, quantise); block mode issues one.
+ */
+int fa_fp8_prep(const void* x, void* x8, float* x_scale, const signed char* signs, int B, int H, int N, int d,
+                unsigned flags, void* stream);
+
+/* Row stride (in elements) of the transposed V produced by fa_fp8_prep:
+ * N rounded up to a multiple of 128.  Returns 0 for N < 1. */
+int fa_fp8_vt_ld(int N);
+
+/*
+ * fa_fwd_fp8 -- exact-attention forward on FP8 E4M3 operands made by
+ * fa_fp8_prep (Q and K rotated with the same signs, V transposed).  Both
+ * products run on FP8 matrix instructions with fp32 accumulation; the
+ * softmax state is fp32 ("FP8 Attention 仍然不等于 FP8 全链路" section of the
+ * FA3 explainer).  Scores are descaled by s_Q,i * s_K,j per block pair; the
+ * V block scale is applied in the PV product.  Probabilities P in (0, 1]
+ * enter the PV product as E4M3(P * 2^7 * mu_j), mu_j the mantissa in
+ * [1, 2) of the key block's V scale, whose exponent goes to the matrix
+ * instruction's power-of-two block scale; l sums the unrounded P.
+ *
+ *   q8, k8  : uint8 [B, H, N, d]
+ *   v8t     : uint8 [B, H, d, fa_fp8_vt_ld(N)] (padding columns must be 0)
+ *   q_scale, k_scale, v_scale : fp32 [B, H, ceil(N / 128)], positive
+ *             normal floats
+ *   o, lse  : as in fa_fwd_bf16
+ *   d       : 128.
+ */
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* q_scale, const float* k_scale,
+               const float* v_scale, float* o, float* lse, int B, int H, int N, int d, int causal,
+               float softmax_scale, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* fa_status_string(int status);
+
+/* FA_ABI_VERSION of the built library. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_FA_H */

@@ -1,0 +1,81 @@
+// Test-only probes of gfx950 builtins whose lane layout or rounding the
+// attention kernels rely on.  Each probe runs one wave over a few KB of
+// caller-provided device buffers; every index stays inside them.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// a, b: 64 lanes x 8 bf16 (raw per-lane operands); c: 64 lanes x 16 f32
+__global__ void k_mfma_bf16(const bf16x8* a, const bf16x8* b, f32x16* c) {
+  const int l = threadIdx.x;
+  c[l] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[l], b[l], f32x16{}, 0, 0, 0);
+}
+
+// a, b: 64 lanes x 32 bytes; c: 64 lanes x 16 f32; E8M0 scales
+__global__ void k_mfma_fp8(const i32x8* a, const i32x8* b, f32x16* c, int sa, int sb) {
+  const int l = threadIdx.x;
+  c[l] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[l], b[l], f32x16{}, 0, 0, 0, sa, 0, sb);
+}
+
+__global__ void k_mfma_fp8_unscaled(const i32x8* a, const i32x8* b, f32x16* c) {
+  const int l = threadIdx.x;
+  c[l] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[l], b[l], f32x16{}, 0, 0, 0, 0, 0, 0);
+}
+
+// x: 4 floats per thread -> one dword of 4 E4M3 codes (bytes in order)
+__global__ void k_cvt_fp8(const float* x, uint32_t* out, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * i], x[4 * i + 1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * i + 2], x[4 * i + 3], w, true);
+  out[i] = w;
+}
+
+// x: 64 floats -> y[l] = x[l ^ 32] via the shuffle the kernels use
+__global__ void k_swap_halves(const float* x, float* y) {
+  const int l = threadIdx.x;
+  y[l] = __shfl_xor(x[l], 32, 64);
+}
+
+// transposed LDS read: LDS holds u16 values 0..1023; lane l reads at byte
+// offset addr[l] (caller keeps addr[l] + 8 <= 2048); out: 64 x 4 u16
+__global__ void k_tr16(const int* addr, short* out) {
+  __shared__ short lds[1024];
+  const int l = threadIdx.x;
+  for (int i = l; i < 1024; i += 64) lds[i] = (short)i;
+  __syncthreads();
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)((__attribute__((address_space(3))) char*)lds + addr[l]));
+  for (int e = 0; e < 4; ++e) out[4 * l + e] = r[e];
+}
+
+extern "C" {
+int probe_mfma_bf16(const void* a, const void* b, float* c, void* s) {
+  hipLaunchKernelGGL(k_mfma_bf16, dim3(1), dim3(64), 0, (hipStream_t)s, (const bf16x8*)a, (const bf16x8*)b, (f32x16*)c);
+  return hipGetLastError();
+}
+int probe_mfma_fp8(const void* a, const void* b, float* c, int sa, int sb, void* s) {
+  hipLaunchKernelGGL(k_mfma_fp8, dim3(1), dim3(64), 0, (hipStream_t)s, (const i32x8*)a, (const i32x8*)b, (f32x16*)c, sa, sb);
+  return hipGetLastError();
+}
+int probe_mfma_fp8_unscaled(const void* a, const void* b, float* c, void* s) {
+  hipLaunchKernelGGL(k_mfma_fp8_unscaled, dim3(1), dim3(64), 0, (hipStream_t)s, (const i32x8*)a, (const i32x8*)b, (f32x16*)c);
+  return hipGetLastError();
+}
+int probe_cvt_fp8(const float* x, uint32_t* out, int n, void* s) {
+  hipLaunchKernelGGL(k_cvt_fp8, dim3((n + 255) / 256), dim3(256), 0, (hipStream_t)s, x, out, n);
+  return hipGetLastError();
+}
+int probe_swap_halves(const float* x, float* y, void* s) {
+  hipLaunchKernelGGL(k_swap_halves, dim3(1), dim3(64), 0, (hipStream_t)s, x, y);
+  return hipGetLastError();
+}
+int probe_tr16(const int* addr, short* out, void* s) {
+  hipLaunchKernelGGL(k_tr16, dim3(1), dim3(64), 0, (hipStream_t)s, addr, out);
+  return hipGetLastError();
+}
+}

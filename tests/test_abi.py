@@ -1,0 +1,80 @@
+"""The C-ABI library loads, exports every function include/fa.h declares, and
+rejects invalid arguments before touching any device (runs without a GPU:
+the pointers below are never dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_attention_73_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+FAKE = 0x10000  # aligned, never dereferenced (validation fails first)
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(fa_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_the_documented_entry_points():
+    assert _declared() == sorted(_lib.SIGNATURES)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strings(lib):
+    assert lib.fa_abi_version() == 1
+    for st in range(-8, 1):
+        assert lib.fa_status_string(st)
+    assert lib.fa_fp8_vt_ld(1) == 128 and lib.fa_fp8_vt_ld(128) == 128 and lib.fa_fp8_vt_ld(129) == 256
+    assert lib.fa_fp8_vt_ld(0) == 0
+
+
+def _bf16(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, l=FAKE, B=1, H=1, N=16, d=128, causal=0, scale=0.125):
+    return lib.fa_fwd_bf16(q, k, v, o, l, B, H, N, d, causal, scale, None)
+
+
+def test_bf16_validation(lib):
+    assert _bf16(lib, q=None) == -1
+    assert _bf16(lib, l=None) == -1
+    assert _bf16(lib, B=0) == -2 and _bf16(lib, N=0) == -2 and _bf16(lib, H=-1) == -2
+    assert _bf16(lib, B=1 << 20, H=1 << 10, N=1 << 10) == -2  # 2^40 * d elements
+    assert _bf16(lib, d=96) == -3 and _bf16(lib, d=32) == -3
+    assert _bf16(lib, causal=2) == -4
+    assert _bf16(lib, scale=0.0) == -4 and _bf16(lib, scale=float("inf")) == -4 and _bf16(lib, scale=-1.0) == -4
+    assert _bf16(lib, q=FAKE + 8) == -5 and _bf16(lib, o=FAKE + 4) == -5
+
+
+def test_fp8_validation(lib):
+    f = lambda **kw: lib.fa_fwd_fp8(kw.get("q", FAKE), FAKE, FAKE, FAKE, FAKE, kw.get("vs", FAKE), FAKE, FAKE,
+                                    kw.get("B", 1), 1, 64, kw.get("d", 128), kw.get("causal", 0),
+                                    kw.get("scale", 0.1), None)
+    assert f(q=None) == -1 and f(vs=None) == -1
+    assert f(B=0) == -2
+    assert f(d=64) == -3
+    assert f(causal=-1) == -4 and f(scale=float("nan")) == -4
+    assert f(q=FAKE + 1) == -5
+    p = lambda **kw: lib.fa_fp8_prep(kw.get("x", FAKE), FAKE, FAKE, None, 1, 1, kw.get("N", 64), kw.get("d", 128),
+                                     kw.get("flags", 0), None)
+    assert p(x=None) == -1 and p(N=0) == -2 and p(d=256) == -3 and p(flags=4) == -4 and p(x=FAKE + 2) == -5
+
+
+def test_valid_call_without_gpu_reports_device_error(lib):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: the device check passes there")
+    assert _bf16(lib) == -6

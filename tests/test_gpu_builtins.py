@@ -1,0 +1,141 @@
+"""In-bounds checks of the gfx950 builtins whose lane layout or rounding the
+kernels depend on (one wave each, a few KB of buffers)."""
+
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import e4m3_decode, e4m3_encode
+
+pytestmark = pytest.mark.gpu
+
+LIB = os.path.join(os.path.dirname(__file__), "hip", "libprobes.so")
+
+
+@pytest.fixture(scope="module")
+def probes():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test collected on a machine without a GPU")
+    lib = ctypes.CDLL(LIB)
+    for n in ("probe_mfma_bf16", "probe_mfma_fp8", "probe_mfma_fp8_unscaled", "probe_cvt_fp8", "probe_swap_halves",
+              "probe_tr16"):
+        getattr(lib, n).restype = ctypes.c_int
+    return lib
+
+
+def _s():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def test_mfma_bf16_32x32x16_layout(probes):
+    g = torch.Generator().manual_seed(1)
+    A = torch.randn(32, 16, generator=g).to(torch.bfloat16)
+    B = torch.randn(16, 32, generator=g).to(torch.bfloat16)
+    a = torch.empty(64, 8, dtype=torch.bfloat16)
+    b = torch.empty(64, 8, dtype=torch.bfloat16)
+    for l in range(64):
+        a[l] = A[l % 32, 8 * (l // 32): 8 * (l // 32) + 8]
+        b[l] = B[8 * (l // 32): 8 * (l // 32) + 8, l % 32]
+    c = torch.zeros(64, 16, dtype=torch.float32, device="cuda")
+    assert probes.probe_mfma_bf16(_p(a.cuda()), _p(b.cuda()), _p(c), _s()) == 0
+    torch.cuda.synchronize()
+    c = c.cpu().numpy()
+    ref = A.double().numpy() @ B.double().numpy()
+    got = np.zeros((32, 32))
+    for l in range(64):
+        for r in range(16):
+            got[8 * (r // 4) + 4 * (l // 32) + (r % 4), l % 32] = c[l, r]
+    np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("sa,sb", [(127, 127), (120, 130), (133, 120)])
+def test_mfma_fp8_32x32x64_layout_and_scales(probes, sa, sb):
+    rng = np.random.default_rng(sa * 1000 + sb)
+    A = rng.integers(0, 256, size=(32, 64)).astype(np.uint8)
+    B = rng.integers(0, 256, size=(64, 32)).astype(np.uint8)
+    A[(A & 0x7F) == 0x7F] = 0x38  # no NaN codes
+    B[(B & 0x7F) == 0x7F] = 0x38
+    a = np.zeros((64, 32), np.uint8)
+    b = np.zeros((64, 32), np.uint8)
+    for l in range(64):
+        a[l] = A[l % 32, 32 * (l // 32): 32 * (l // 32) + 32]
+        b[l] = B[32 * (l // 32): 32 * (l // 32) + 32, l % 32]
+    c = torch.zeros(64, 16, dtype=torch.float32, device="cuda")
+    ta, tb = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+    assert probes.probe_mfma_fp8(_p(ta), _p(tb), _p(c), sa, sb, _s()) == 0
+    torch.cuda.synchronize()
+    c = c.cpu().numpy()
+    ref = (e4m3_decode(A) @ e4m3_decode(B)) * 2.0 ** (sa - 127) * 2.0 ** (sb - 127)
+    got = np.zeros((32, 32))
+    for l in range(64):
+        for r in range(16):
+            got[8 * (r // 4) + 4 * (l // 32) + (r % 4), l % 32] = c[l, r]
+    np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-3 * np.abs(ref).max())
+
+
+def test_mfma_fp8_unscaled_form(probes):
+    # scale operands 0 select the plain instruction; record what it computes
+    rng = np.random.default_rng(7)
+    A = (rng.integers(0, 2, size=(32, 64)) * 0x38).astype(np.uint8)  # 0 or 1.0
+    B = (rng.integers(0, 2, size=(64, 32)) * 0x38).astype(np.uint8)
+    a = np.zeros((64, 32), np.uint8)
+    b = np.zeros((64, 32), np.uint8)
+    for l in range(64):
+        a[l] = A[l % 32, 32 * (l // 32): 32 * (l // 32) + 32]
+        b[l] = B[32 * (l // 32): 32 * (l // 32) + 32, l % 32]
+    c = torch.zeros(64, 16, dtype=torch.float32, device="cuda")
+    assert probes.probe_mfma_fp8_unscaled(_p(torch.from_numpy(a).cuda()), _p(torch.from_numpy(b).cuda()), _p(c), _s()) == 0
+    torch.cuda.synchronize()
+    ref = e4m3_decode(A) @ e4m3_decode(B)
+    got = np.zeros((32, 32))
+    cc = c.cpu().numpy()
+    for l in range(64):
+        for r in range(16):
+            got[8 * (r // 4) + 4 * (l // 32) + (r % 4), l % 32] = cc[l, r]
+    print("unscaled fp8 mfma / exact product ratio:", float(got.sum() / max(ref.sum(), 1)))
+    np.testing.assert_allclose(got, ref, rtol=1e-6)
+
+
+def test_cvt_pk_fp8_rounding_matches_oracle(probes):
+    vals = e4m3_decode(np.arange(127, dtype=np.uint8))
+    mids = (vals[1:] + vals[:-1]) / 2
+    rng = np.random.default_rng(3)
+    x = np.concatenate([vals, -vals, mids, -mids, rng.uniform(-448, 448, 4000), rng.normal(0, 0.01, 4000)])
+    x = x[: (len(x) // 4) * 4].astype(np.float32)
+    n = len(x) // 4
+    out = torch.zeros(n, dtype=torch.int32, device="cuda")
+    assert probes.probe_cvt_fp8(_p(torch.from_numpy(x).cuda()), _p(out), n, _s()) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint8).reshape(-1)
+    np.testing.assert_array_equal(e4m3_decode(got), e4m3_decode(e4m3_encode(x.astype(np.float64))))
+
+
+def test_swap_halves(probes):
+    x = torch.arange(64, dtype=torch.float32, device="cuda")
+    y = torch.zeros(64, dtype=torch.float32, device="cuda")
+    assert probes.probe_swap_halves(_p(x), _p(y), _s()) == 0
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y.cpu().numpy(), np.arange(64) ^ 32)
+
+
+def test_ds_read_tr16_b64_mapping(probes):
+    # informational: record which LDS element each lane receives when lane l
+    # addresses the 64-bit row at byte 8 l
+    addr = torch.arange(64, dtype=torch.int32, device="cuda") * 8
+    out = torch.zeros(64 * 4, dtype=torch.int16, device="cuda")
+    assert probes.probe_tr16(_p(addr), _p(out), _s()) == 0
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().reshape(64, 4)
+    os.makedirs("gpurun_out", exist_ok=True)
+    with open("gpurun_out/tr16_mapping.txt", "w") as f:
+        for l in range(64):
+            f.write(f"{l}: {list(map(int, o[l]))}\n")
+    print("tr16 lane 0..3:", o[:4].tolist())
+    assert o.min() >= 0 and o.max() < 256
