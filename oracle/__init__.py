@@ -43,4 +43,5 @@ from .fp8 import (  # noqa: F401
     fp8_attention_emulate,
     fp8_emulate,
     scale_mantissa,
+    pow2_ceil,
 )

@@ -14,9 +14,15 @@ What the pages fix, and the readings taken where they are silent:
   (batch, head), all of d (P1 section "Block Quantization 为什么优于
   Per-Tensor Scale" keeps one scale per B_r x d or B_c x d tile; the block
   height of 128 is the plain choice for tiles of 128 query rows).  The scale
-  formula was lost from the page text; s = amax / 448, and s = 1 for an
-  all-zero block.  Per-tensor mode uses one amax over the whole tensor (the
-  same section's baseline, one scale for all of Q).
+  formula was lost from the page text; s = amax / 448 for Q and K, and s = 1
+  for an all-zero block.  For V, the operand of the PV product, s is the
+  power of two 2^ceil(log2(amax / 448)): the matrix instruction's E8M0
+  block exponent then carries it exactly, its codes are exact in any
+  precision, and the largest probability (P = 1) maps to a representable
+  value instead of landing on an E4M3 rounding tie (with s = amax / 448 and
+  bf16 amax, 2^7 * mantissa(s) often is a tie, e.g. 232 between 224 and
+  240).  Per-tensor mode uses one amax over the whole tensor (the same
+  section's baseline, one scale for all of Q).
 * Incoherent processing: Q and K are both multiplied by the same random
   orthogonal matrix M = diag(sigma) H_d / sqrt(d), sigma a per-head vector of
   +-1 and H_d the Sylvester Hadamard matrix (P1 section "Incoherent
@@ -56,6 +62,7 @@ __all__ = [
     "fp8_attention_emulate",
     "fp8_emulate",
     "scale_mantissa",
+    "pow2_ceil",
 ]
 
 E4M3_MAX = 448.0  # P2 section 三.3
@@ -123,17 +130,38 @@ def rotation_matrix(signs) -> np.ndarray:
     return (s[:, None] * hadamard_matrix(d)) / np.sqrt(d)
 
 
-def _rotate(x: np.ndarray, signs) -> np.ndarray:
-    """y[b, h] = x[b, h] @ M_h with one rotation per head."""
+def _rotate_unnormalised(x: np.ndarray, signs) -> np.ndarray:
+    """y[b, h] = x[b, h] @ (diag(sigma_h) H_d): the rotation without its
+    1/sqrt(d).  For bf16 inputs every entry is a sum of d signed bf16
+    values, which float64 holds exactly for the value ranges used here."""
     signs = np.asarray(signs)
     y = np.empty_like(x)
+    Hd = hadamard_matrix(x.shape[-1]).astype(np.float64)
     for h in range(x.shape[1]):
-        y[:, h] = x[:, h] @ rotation_matrix(signs[h])
+        y[:, h] = x[:, h] @ (np.asarray(signs[h], dtype=np.float64)[:, None] * Hd)
     return y
 
 
-def quantize_fp8(x, signs=None, per_tensor: bool = False, block: int = SCALE_BLOCK, quantize: bool = True):
+def pow2_ceil(x) -> np.ndarray:
+    """Smallest power of two >= x, for positive x (exact: frexp is exact)."""
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))  # x = m * 2^e, m in [0.5, 1)
+    return np.where(m == 0.5, np.ldexp(1.0, e - 1), np.ldexp(1.0, e))
+
+
+def quantize_fp8(x, signs=None, per_tensor: bool = False, block: int = SCALE_BLOCK, quantize: bool = True,
+                 pow2: bool = False):
     """Rotate (optionally), scale and round one tensor ``[B, H, N, d]`` to E4M3.
+
+    With u = x diag(sigma) H_d (unnormalised; u = x without rotation) and
+    r = sqrt(d) (1 without rotation), the rotated tensor is y = u / r, the
+    block amax is a = max |u| / r and the scale s = a / 448.  The code is
+    RNE(y / s) = RNE(u * 448 / max|u|); that value decides an integer, so it
+    is taken in float32 exactly as the kernel forms it (the pages fix no
+    precision): code = E4M3(clamp(fl32(fl32(u) * fl32(448 / fl32(max|u|))))).
+
+    With ``pow2`` (the PV operand V; no rotation) the scale is the power of
+    two s = 2^ceil(log2(a / 448)), the smallest one with a / s <= 448, and the
+    code RNE(y / s) is exact in any precision.
 
     Returns ``(codes, scale, y)``:
       codes uint8 ``[B, H, N, d]`` (None when ``quantize`` is False),
@@ -142,20 +170,33 @@ def quantize_fp8(x, signs=None, per_tensor: bool = False, block: int = SCALE_BLO
     """
     x = to_f64(x)
     B, H, N, d = x.shape
-    y = _rotate(x, signs) if signs is not None else x.copy()
+    rot = signs is not None
+    u = _rotate_unnormalised(x, signs) if rot else x.copy()
+    r = np.sqrt(d) if rot else 1.0
+    y = u / r
     nb = -(-N // block)
-    scale = np.empty((B, H, nb))
+    amax = np.empty((B, H, nb))
     if per_tensor:
-        a = np.abs(y).max() if y.size else 0.0
-        scale[:] = a / E4M3_MAX if a > 0 else 1.0
+        amax[:] = np.abs(u).max() if u.size else 0.0
     else:
         for i in range(nb):
-            a = np.abs(y[:, :, i * block:(i + 1) * block, :]).max(axis=(2, 3))
-            scale[:, :, i] = np.where(a > 0, a / E4M3_MAX, 1.0)
+            amax[:, :, i] = np.abs(u[:, :, i * block:(i + 1) * block, :]).max(axis=(2, 3))
+    if pow2:
+        if rot:
+            raise ValueError("power-of-two scales are for the unrotated V operand")
+        scale = np.where(amax > 0, pow2_ceil(amax / E4M3_MAX), 1.0)
+        if not quantize:
+            return None, scale, y
+        s_rows = np.repeat(scale, block, axis=2)[:, :, :N, None]
+        return e4m3_encode(np.clip(y / s_rows, -E4M3_MAX, E4M3_MAX)), scale, y
+    scale = np.where(amax > 0, amax / (E4M3_MAX * r), 1.0)
     if not quantize:
         return None, scale, y
-    s_rows = np.repeat(scale, block, axis=2)[:, :, :N, None]
-    codes = e4m3_encode(np.clip(y / s_rows, -E4M3_MAX, E4M3_MAX))
+    a32 = np.repeat(amax, block, axis=2)[:, :, :N, None].astype(np.float32)
+    with np.errstate(divide="ignore"):
+        inv32 = np.where(a32 > 0, np.float32(E4M3_MAX) / a32, np.float32(0)).astype(np.float32)
+    q32 = (u.astype(np.float32) * inv32).astype(np.float32)
+    codes = e4m3_encode(np.clip(q32.astype(np.float64), -E4M3_MAX, E4M3_MAX))
     return codes, scale, y
 
 
@@ -242,8 +283,8 @@ def fp8_emulate(q, k, v, signs=None, mode: str = "block+had", causal: bool = Fal
     rot = signs if mode == "block+had" else None
     per_tensor = mode == "tensor"
     out = []
-    for x, sg in ((q, rot), (k, rot), (v, None)):
-        codes, s, y = quantize_fp8(x, signs=sg, per_tensor=per_tensor, quantize=quantize)
+    for x, sg, p2 in ((q, rot, False), (k, rot, False), (v, None, True)):
+        codes, s, y = quantize_fp8(x, signs=sg, per_tensor=per_tensor, quantize=quantize, pow2=p2)
         out.append((dequantize_fp8(codes, s) if quantize else y, s))
     (qh, _), (kh, _), (vh, vs) = out
     return fp8_attention_emulate(qh, kh, vh, causal=causal, scale=scale, Bc=Bc, quantize_p=quantize, v_scale=vs)
