@@ -141,9 +141,9 @@ def main():
         signs = make_signs(w8.H, w8.d, w8.seed + 1).to(dev)
         q8, qs_ = fa.fp8_prep(q, signs=signs)
         k8, ks_ = fa.fp8_prep(k, signs=signs)
-        v8t, vs_ = fa.fp8_prep(v, transpose=True)
+        v8t, vs_ = fa.fp8_prep_v(v)
         t_prep, _ = _time_launches(lambda: fa.fp8_prep(q, signs=signs), 20, 3)
-        t_prep_v, _ = _time_launches(lambda: fa.fp8_prep(v, transpose=True), 20, 3)
+        t_prep_v, _ = _time_launches(lambda: fa.fp8_prep_v(v), 20, 3)
         t8, _ = _time_launches(lambda: fa.fwd_fp8(q8, k8, v8t, qs_, ks_, vs_), 20, 3)
         elems = w8.B * w8.H * w8.N * w8.d
         prep_bytes = elems * 2 + elems + w8.B * w8.H * ((w8.N + 127) // 128) * 4

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
 
 FA_PREP_TRANSPOSE = 1
 FA_PREP_PER_TENSOR = 2
+FA_PREP_POW2_SCALE = 4
 
 # every function the header declares, with its ctypes signature
 _VP, _FP, _I, _F = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
@@ -94,10 +95,11 @@ def fp8_vt_ld(N: int) -> int:
     return int(load().fa_fp8_vt_ld(int(N)))
 
 
-def fp8_prep(x, signs=None, transpose: bool = False, per_tensor: bool = False):
+def fp8_prep(x, signs=None, transpose: bool = False, per_tensor: bool = False, pow2_scale: bool = False):
     """E4M3 codes and per-128-row scales of one bf16 ``[B, H, N, d]`` tensor.
 
     ``signs``: int8 ``[H, d]`` of +-1 on the GPU (rotate, for Q and K) or None.
+    For V use ``transpose=True, pow2_scale=True`` (:func:`fp8_prep_v`).
     Returns ``(x8, scale)``: uint8 ``[B, H, N, d]`` (or ``[B, H, d, ld]`` when
     ``transpose``) and fp32 ``[B, H, ceil(N / 128)]``.
     """
@@ -111,11 +113,17 @@ def fp8_prep(x, signs=None, transpose: bool = False, per_tensor: bool = False):
     shape = (B, H, d, fp8_vt_ld(N)) if transpose else (B, H, N, d)
     x8 = torch.empty(shape, dtype=torch.uint8, device=x.device)
     sc = torch.empty((B, H, nb), dtype=torch.float32, device=x.device)
-    flags = (FA_PREP_TRANSPOSE if transpose else 0) | (FA_PREP_PER_TENSOR if per_tensor else 0)
+    flags = ((FA_PREP_TRANSPOSE if transpose else 0) | (FA_PREP_PER_TENSOR if per_tensor else 0)
+             | (FA_PREP_POW2_SCALE if pow2_scale else 0))
     st = load().fa_fp8_prep(x.data_ptr(), x8.data_ptr(), sc.data_ptr(), None if signs is None else signs.data_ptr(),
                             B, H, N, d, flags, _stream(x))
     _check("fa_fp8_prep", st)
     return x8, sc
+
+
+def fp8_prep_v(v, per_tensor: bool = False):
+    """The PV operand: V transposed with power-of-two block scales."""
+    return fp8_prep(v, transpose=True, per_tensor=per_tensor, pow2_scale=True)
 
 
 def fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, causal: bool = False, softmax_scale: float | None = None,

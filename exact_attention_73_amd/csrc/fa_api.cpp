@@ -107,7 +107,8 @@ int fa_fp8_prep(const void* x, void* x8, float* x_scale, const signed char* sign
   if (!x || !x8 || !x_scale) return FA_ERR_NULL_PTR;
   if (int e = check_shape(B, H, N, d == 128 ? d : 1)) return e;
   if (d != 128) return FA_ERR_HEADDIM;
-  if (flags & ~(FA_PREP_TRANSPOSE | FA_PREP_PER_TENSOR)) return FA_ERR_ARG;
+  if (flags & ~(FA_PREP_TRANSPOSE | FA_PREP_PER_TENSOR | FA_PREP_POW2_SCALE)) return FA_ERR_ARG;
+  if ((flags & FA_PREP_POW2_SCALE) && signs) return FA_ERR_ARG;
   if (!aligned16(x) || !aligned16(x8) || !aligned16(x_scale)) return FA_ERR_ALIGN;
   if (int e = check_device()) return e;
 
@@ -122,6 +123,7 @@ int fa_fp8_prep(const void* x, void* x8, float* x_scale, const signed char* sign
   p.ld = fa_fp8_vt_ld(N);
   p.transpose = (flags & FA_PREP_TRANSPOSE) != 0;
   p.per_tensor = (flags & FA_PREP_PER_TENSOR) != 0;
+  p.pow2 = (flags & FA_PREP_POW2_SCALE) != 0;
   return launch_status(fa::launch_fp8_prep(p, d, static_cast<hipStream_t>(stream)));
 }
 

@@ -108,22 +108,35 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8PrepParams p) {
   }
 
   const float norm = rot ? 11.313708498984761f : 1.f;  // sqrt(128)
-  float inv;  // multiplier turning y into the E4M3 range
   if (MODE == kPrepGlobalScale) {
-    inv = 1.f / (p.scale[0] * norm);
-  } else {
+    // the tensor's amax = max over every block amax left by the first pass
+    amax = 0.f;
+    const int n = (int)gridDim.x;
+    for (int i = tid; i < n; i += 256) amax = __builtin_fmaxf(amax, p.scale[i]);
+  }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off, 64));
-    if ((tid & 63) == 0) red[tid >> 6] = amax;
-    __syncthreads();
-    amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
-    if (MODE == kPrepAmaxOnly) {
-      if (tid == 0) p.scale[blockIdx.x] = amax;  // raw amax of y; turned into s by the reduce kernel
-      return;
-    }
-    if (tid == 0) p.scale[blockIdx.x] = amax > 0.f ? amax / (kE4M3Max * norm) : 1.f;
+  for (int off = 32; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+  if (MODE == kPrepAmaxOnly) {
+    if (tid == 0) p.scale[blockIdx.x] = amax;  // raw block amax of y; the scales are written last
+    return;
+  }
+  // multiplier turning y into the E4M3 range; the same expression in both modes
+  float inv, s_out;
+  if (p.pow2) {
+    // s = 2^k, k = ceil(log2(amax / 448)) from the bits of amax (448 = 1.75 * 2^8)
+    const uint32_t ab = __float_as_uint(amax);
+    int k = (int)((ab >> 23) & 0xffu) - 127 - 8 + ((ab & 0x7fffffu) > 0x600000u ? 1 : 0);
+    k = max(k, -126);
+    s_out = amax > 0.f ? __uint_as_float((uint32_t)(k + 127) << 23) : 1.f;
+    inv = amax > 0.f ? __uint_as_float((uint32_t)(127 - k) << 23) : 0.f;  // exact 2^-k
+  } else {
+    s_out = amax > 0.f ? amax / (kE4M3Max * norm) : 1.f;
     inv = amax > 0.f ? kE4M3Max / amax : 0.f;
   }
+  if (MODE == kPrepFused && tid == 0) p.scale[blockIdx.x] = s_out;
 
   if (!p.transpose) {
     uint8_t* Y = p.x8 + (size_t)bh * p.N * D;
@@ -159,8 +172,9 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8PrepParams p) {
   }
 }
 
-// Global amax over all block amaxes -> one scale written to every entry.
-__global__ __launch_bounds__(1024) void fp8_tensor_scale_kernel(float* scale, int n, float norm) {
+// Global amax over all block amaxes -> one scale written to every entry
+// (runs after the quantising pass, which reads the block amaxes).
+__global__ __launch_bounds__(1024) void fp8_tensor_scale_kernel(float* scale, int n, float norm, bool pow2) {
   __shared__ float red[16];
   float a = 0.f;
   for (int i = threadIdx.x; i < n; i += 1024) a = __builtin_fmaxf(a, scale[i]);
@@ -171,7 +185,12 @@ __global__ __launch_bounds__(1024) void fp8_tensor_scale_kernel(float* scale, in
   a = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) a = __builtin_fmaxf(a, red[i]);
-  const float s = a > 0.f ? a / (kE4M3Max * norm) : 1.f;
+  float s = a > 0.f ? a / (kE4M3Max * norm) : 1.f;
+  if (pow2 && a > 0.f) {
+    const uint32_t ab = __float_as_uint(a);
+    const int k = max((int)((ab >> 23) & 0xffu) - 127 - 8 + ((ab & 0x7fffffu) > 0x600000u ? 1 : 0), -126);
+    s = __uint_as_float((uint32_t)(k + 127) << 23);
+  }
   __syncthreads();
   for (int i = threadIdx.x; i < n; i += 1024) scale[i] = s;
 }
@@ -402,9 +421,9 @@ hipError_t launch_fp8_prep(const Fp8PrepParams& p, int d, hipStream_t stream) {
     return hipGetLastError();
   }
   hipLaunchKernelGGL(fp8_prep_kernel<kPrepAmaxOnly>, dim3(grid), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL(fp8_tensor_scale_kernel, dim3(1), dim3(1024), 0, stream, p.scale, (int)grid,
-                     p.signs ? 11.313708498984761f : 1.f);
   hipLaunchKernelGGL(fp8_prep_kernel<kPrepGlobalScale>, dim3(grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(fp8_tensor_scale_kernel, dim3(1), dim3(1024), 0, stream, p.scale, (int)grid,
+                     p.signs ? 11.313708498984761f : 1.f, p.pow2);
   return hipGetLastError();
 }
 

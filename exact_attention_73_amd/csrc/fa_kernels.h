@@ -29,6 +29,7 @@ struct Fp8PrepParams {
   int B, H, N, ld;
   bool transpose;
   bool per_tensor;
+  bool pow2;  // power-of-two scales (no rotation)
 };
 
 hipError_t launch_fp8_prep(const Fp8PrepParams& p, int d, hipStream_t stream);

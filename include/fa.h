@@ -57,6 +57,7 @@ enum fa_status {
 /* Flags of fa_fp8_prep. */
 #define FA_PREP_TRANSPOSE 1u  /* write x8 transposed, [B, H, d, fa_fp8_vt_ld(N)]       */
 #define FA_PREP_PER_TENSOR 2u /* one scale for the whole tensor (the comparison mode) */
+#define FA_PREP_POW2_SCALE 4u /* power-of-two scales (for V, the PV operand); no rotation */
 
 /*
  * fa_fwd_bf16 -- exact attention forward, bf16 operands, fp32 accumulation.
@@ -90,15 +91,22 @@ int fa_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* ls
  *             N..ld-1 are written as zero codes.
  *   x_scale : fp32 [B, H, ceil(N / 128)]: s = amax(|y|) / 448 over each block
  *             of 128 rows (all of d); s = 1 for an all-zero block.  With
- *             FA_PREP_PER_TENSOR, amax runs over the whole tensor and every
- *             entry holds the same s.
+ *             FA_PREP_POW2_SCALE, s = 2^ceil(log2(amax / 448)) instead (the
+ *             smallest power of two with amax / s <= 448), which is what V
+ *             should use: the PV product then takes s as an exact block
+ *             exponent.  With FA_PREP_PER_TENSOR, amax runs over the whole
+ *             tensor and every entry holds the same s.
  *   d       : 128.
- *   flags   : OR of FA_PREP_TRANSPOSE and FA_PREP_PER_TENSOR (FA_ERR_ARG for
- *             any other bit).
+ *   flags   : OR of FA_PREP_TRANSPOSE, FA_PREP_PER_TENSOR and
+ *             FA_PREP_POW2_SCALE (FA_ERR_ARG for any other bit, or for
+ *             FA_PREP_POW2_SCALE together with signs).
  *
- * Codes are round-to-nearest-even of clamp(y * 448 / amax, -448, 448).
- * Per-tensor mode issues three kernels on `stream` (block amax, global
- * amax, quantise); block mode issues one.
+ * Codes are round-to-nearest-even of clamp(y * 448 / amax, -448, 448), the
+ * product formed in fp32; with FA_PREP_POW2_SCALE of y / s (exact).
+ * Per-tensor mode issues three kernels on `stream` (block amaxes into
+ * x_scale, quantise with the tensor amax reduced from them, then the
+ * scales); block mode issues one.  Calls that share an x_scale buffer
+ * must be ordered on one stream.
  */
 int fa_fp8_prep(const void* x, void* x8, float* x_scale, const signed char* signs, int B, int H, int N, int d,
                 unsigned flags, void* stream);
@@ -121,7 +129,8 @@ int fa_fp8_vt_ld(int N);
  *   q8, k8  : uint8 [B, H, N, d]
  *   v8t     : uint8 [B, H, d, fa_fp8_vt_ld(N)] (padding columns must be 0)
  *   q_scale, k_scale, v_scale : fp32 [B, H, ceil(N / 128)], positive
- *             normal floats
+ *             normal floats (v_scale from FA_PREP_POW2_SCALE, so that
+ *             mu_j = 1; other positive scales are accepted)
  *   o, lse  : as in fa_fwd_bf16
  *   d       : 128.
  */

@@ -67,9 +67,10 @@ def test_fp8_validation(lib):
     assert f(d=64) == -3
     assert f(causal=-1) == -4 and f(scale=float("nan")) == -4
     assert f(q=FAKE + 1) == -5
-    p = lambda **kw: lib.fa_fp8_prep(kw.get("x", FAKE), FAKE, FAKE, None, 1, 1, kw.get("N", 64), kw.get("d", 128),
-                                     kw.get("flags", 0), None)
-    assert p(x=None) == -1 and p(N=0) == -2 and p(d=256) == -3 and p(flags=4) == -4 and p(x=FAKE + 2) == -5
+    p = lambda **kw: lib.fa_fp8_prep(kw.get("x", FAKE), FAKE, FAKE, kw.get("signs", None), 1, 1, kw.get("N", 64),
+                                     kw.get("d", 128), kw.get("flags", 0), None)
+    assert p(x=None) == -1 and p(N=0) == -2 and p(d=256) == -3 and p(flags=8) == -4 and p(x=FAKE + 2) == -5
+    assert p(flags=4, signs=FAKE) == -4  # power-of-two scales are for the unrotated V operand
 
 
 def test_valid_call_without_gpu_reports_device_error(lib):
