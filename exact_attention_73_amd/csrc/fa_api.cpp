@@ -43,6 +43,8 @@ int check_shape(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
   const double elems = (double)B * (double)H * (double)N * (double)d;
   if (elems >= 1099511627776.0) return FA_ERR_SHAPE;  // 2^40
+  // one (batch, head) slice is addressed with 32-bit byte offsets
+  if ((double)N * (double)d * 2.0 >= 2147483648.0) return FA_ERR_SHAPE;
   // the grid is B * H * ceil(N / 128) workgroups
   if ((double)B * (double)H * (double)((N + 127) / 128) >= 2147483647.0) return FA_ERR_SHAPE;
   return FA_OK;

@@ -5,35 +5,46 @@
 // l, rescaled accumulator; wmrh.cn FlashAttention V3 article, section 二.1;
 // FA3 explainer "FlashAttention-3：用异步流水榨出 Hopper 的 Attention 性能",
 // section "Online Softmax 仍是精确合并的核心").  The N x N score matrix only
-// ever exists as one 32 x 32 register tile per matrix instruction.
+// ever exists as 32 x 32 register tiles.
 //
 // Work decomposition (FA3 explainer, section "FA2 到 H100 后，瓶颈为什么又变了":
 // parallelism over batch, heads and query tiles): one workgroup of 4 waves
-// per (batch, head, 128-row query tile); each wave owns 32 query rows.
+// per (batch, head, 128-row query tile); each wave owns 32 query rows; two
+// workgroups share a CU, so every SIMD interleaves two waves.
 //
 // Per wave the products are computed transposed, S^T = K Q^T and
 // O^T = V^T P^T, so that a lane owns ONE query row (column L & 31 of every
 // accumulator) and 16 of the 32 keys of each 32-key block.  The row max is
-// then 31 in-lane max operations plus one exchange with the other half
-// wave, the row sum needs no exchange until the epilogue, and the S^T
-// accumulator registers are, after the exp and the bf16 cast, exactly the
-// B operand of the PV product (the key permutation they carry is matched by
-// the layout of V in LDS, the same trick the FA3 explainer's section
-// "FP8 路径的第一个问题：WGMMA Layout" describes for P and V).
+// then in-lane max operations plus one exchange with the other half wave,
+// the row sum needs no exchange until the epilogue, and the S^T accumulator
+// registers are, after exp2 and the bf16 cast, exactly the B operand of the
+// PV product; the key permutation they carry is matched by how V^T is read
+// (the FA3 explainer's section "FP8 路径的第一个问题：WGMMA Layout" describes
+// the same trick of matching P's column order with V's row order).
 //
-// Data path per key tile j (FA3 explainer, sections "第一层重叠" and
-// "Circular Buffer 为什么不能无限加深"): K_j and V_j are read from HBM once
-// per workgroup into a 2-stage LDS ring (stage = j mod 2) while tile j-1 is
-// being consumed (the next tile's global loads are issued before the PV
-// products of the current one); Q stays in VGPRs for the whole loop.  K is stored
-// row-major with an XOR swizzle of 16-byte chunks (conflict-free A-operand
-// reads), V is stored as [key/4][d][key%4] so that the transposed operand
-// V^T is read with two 8-byte loads per matrix instruction.
+// Data path (FA3 explainer, sections "第一层重叠：Producer 与 Consumer 并行",
+// "Circular Buffer 为什么不能无限加深" and "第三层重叠：单个 Warpgroup 内跨迭代
+// Pipeline"): K and V tiles go from HBM straight into LDS with buffer loads
+// that write LDS directly (no register staging; rows past N read as zero
+// through the buffer range check).  K runs one tile ahead of V: during the
+// step for tile j the workgroup holds K_{j+1} and V_j, and the loads of
+// K_{j+2} and V_{j+1} are in flight, in 2-slot rings (slot = tile mod 2).
+// Inside a wave, S_{j+1} = K_{j+1} Q^T is issued on the matrix cores while
+// the softmax of S_j runs on the vector ALUs (two S buffers, S_cur/S_next).
+// Q stays in VGPRs for the whole loop.  K is stored row-major with an XOR
+// swizzle of 16-byte chunks (conflict-free A-operand reads); V is stored
+// row-major with its own swizzle and read transposed with ds_read_b64_tr_b16.
+//
+// Softmax: exp2 domain (scale * log2 e folded into one FMA per score) and a
+// lazy rescale: the running max used as the exponent reference only moves
+// when some row of the wave has grown by more than 8 (log2 units); P is then
+// at most 2^8 and O, l are rescaled only on those tiles.  O / l is exact
+// whatever reference is used, so this changes no result beyond rounding.
 //
 // Causal (FA3 explainer, section "为什么 Causal Shape 可能更难调度"): a
 // workgroup only visits key tiles up to its last query row, only tiles that
 // cross a wave's diagonal are masked element-wise, waves whose rows all lie
-// above a tile skip it, and the heaviest query tiles are launched first.
+// above a tile skip its products, and the heaviest query tiles launch first.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -44,35 +55,66 @@ constexpr int kWaves = 4;
 constexpr int kQW = 32;              // query rows per wave
 constexpr int kBR = kWaves * kQW;    // query rows per workgroup
 constexpr int kThreads = kWaves * 64;
+constexpr float kLazyLog2 = 8.f;     // rescale only when a row max grows by more than 2^8
 
 template <int D> struct Bf16Cfg;
 template <> struct Bf16Cfg<64> { static constexpr int BC = 64; static constexpr int MINB = 2; };
 template <> struct Bf16Cfg<128> { static constexpr int BC = 64; static constexpr int MINB = 2; };
 template <> struct Bf16Cfg<256> { static constexpr int BC = 32; static constexpr int MINB = 1; };
 
-// XOR applied to the 16-byte chunk index of K row r in LDS: makes the 16
-// rows read together by a ds_read_b128 land on 16 distinct bank groups.
+typedef __attribute__((address_space(3))) void* lds_void_t;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4* lds_i16x4_t;
+
+// XOR applied to the 16-byte chunk index of K row r: the rows read by one
+// ds_read_b128 spread evenly over the LDS banks.
 template <int D> __device__ __forceinline__ int k_swizzle(int r) {
   if constexpr (D == 64) return (r >> 1) & 7;  // 128-byte rows: two rows per 256 bytes
   else return r & 15;
+}
+// XOR for V rows, matched to the transposed read (8 rows x 4 chunks per
+// instruction land on 16 distinct bank groups, twice each).
+template <int D> __device__ __forceinline__ int v_swizzle(int r) {
+  if constexpr (D == 64) return ((r >> 1) & 1) << 2;
+  else return (r & 3) << 2;
+}
+
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 16 bytes per lane from buffer offset voff straight into LDS at dst + 16 * lane
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint16_t* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t)dst, 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// four 16-bit elements through the transposing LDS read
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* src) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t)src);
 }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, Bf16Cfg<D>::MINB) void fwd_bf16_kernel(FwdBf16Params p) {
   constexpr int BC = Bf16Cfg<D>::BC;
-  constexpr int CPR = D / 8;           // 16-byte chunks per row
-  constexpr int KCH = BC * CPR;        // chunks of a K tile
-  constexpr int KPT = KCH / kThreads;  // K chunks per thread
-  constexpr int VUN = (BC / 4) * CPR;  // (key quad, d chunk) units of a V tile
-  constexpr int VPT = (VUN + kThreads - 1) / kThreads;  // V units per thread (the last may be partial)
-  constexpr int NKB = BC / 32;         // 32-key blocks of S^T per tile
-  constexpr int NDB = D / 32;          // 32-row blocks of O^T
-  constexpr int NQS = D / 16;          // k-steps of S^T = K Q^T
-  constexpr int NPS = BC / 16;         // k-steps of O^T = V^T P^T
-  static_assert(KCH % kThreads == 0 && (VUN % kThreads == 0 || VUN < kThreads), "tile must split over the workgroup");
+  constexpr int ROWB = D * 2;                 // bytes per K/V row
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int INSTR = BC * ROWB / 1024;     // 1 KB wave-loads per tile
+  constexpr int IPW = INSTR / kWaves;         // ... per wave
+  constexpr int RPI = 1024 / ROWB;            // rows per wave-load
+  constexpr int NKB = BC / 32;                // 32-key blocks of S^T per tile
+  constexpr int NDB = D / 32;                 // 32-row blocks of O^T
+  constexpr int NQS = D / 16;                 // k-steps of S^T = K Q^T
+  constexpr int NPS = BC / 16;                // k-steps of O^T = V^T P^T
+  static_assert(INSTR % kWaves == 0, "tile must split over the waves");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BC * D];
+  // one LDS object per ring slot, addressed with compile-time slot numbers,
+  // so the compiler can tell the slot being filled from the slots being read
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks0[BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks1[BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs0[BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs1[BC * D];
 
   const int N = p.N;
   const int BH = p.B * p.H;
@@ -91,9 +133,6 @@ __global__ __launch_bounds__(kThreads, Bf16Cfg<D>::MINB) void fwd_bf16_kernel(Fw
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const size_t base = (size_t)bh * N * D;
-  const uint16_t* __restrict__ Qg = p.q + base;
-  const uint16_t* __restrict__ Kg = p.k + base;
-  const uint16_t* __restrict__ Vg = p.v + base;
   const int q0 = qt * kBR + wave * kQW;  // first query row of this wave
   const int qrow = q0 + l32;             // the query row this lane owns
 
@@ -102,10 +141,10 @@ __global__ __launch_bounds__(kThreads, Bf16Cfg<D>::MINB) void fwd_bf16_kernel(Fw
   bf16x8 qreg[NQS];
   {
     const bool ok = qrow < N;
-    const u32x4* src = reinterpret_cast<const u32x4*>(Qg + (size_t)(ok ? qrow : 0) * D);
+    const u32x4* src = reinterpret_cast<const u32x4*>(p.q + base + (size_t)(ok ? qrow : 0) * D);
 #pragma unroll
     for (int s = 0; s < NQS; ++s) {
-      u32x4 t = ok ? src[2 * s + hi] : u32x4{0, 0, 0, 0};
+      const u32x4 t = ok ? src[2 * s + hi] : u32x4{0, 0, 0, 0};
       qreg[s] = __builtin_bit_cast(bf16x8, t);
     }
   }
@@ -113,152 +152,152 @@ __global__ __launch_bounds__(kThreads, Bf16Cfg<D>::MINB) void fwd_bf16_kernel(Fw
   const int kend = CAUSAL ? min(N, qt * kBR + kBR) : N;
   const int ntiles = (kend + BC - 1) / BC;
 
-  u32x4 kpre[KPT];
-  u32x4 vpre[VPT][4];
-
-  auto load_tile = [&](int j) {
-    const int key0 = j * BC;
+  // ---- direct-to-LDS tile loads -------------------------------------------
+  // Wave-load i of wave w fills LDS bytes [(IPW w + i) KB, +1 KB) of the
+  // slot: RPI rows; lane L writes physical chunk L % CPR of row L / CPR and
+  // therefore fetches the logical chunk that the swizzle puts there.
+  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(p.k + base, N * ROWB);
+  const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(p.v + base, N * ROWB);
+  int koff[IPW], voff[IPW];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int ci = tid + kThreads * i, row = ci / CPR, ch = ci % CPR, key = key0 + row;
-      kpre[i] = key < N ? *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + ch * 8) : u32x4{0, 0, 0, 0};
-    }
+  for (int i = 0; i < IPW; ++i) {
+    const int row = (wave * IPW + i) * RPI + lane / CPR, pc = lane % CPR;
+    koff[i] = row * ROWB + ((pc ^ k_swizzle<D>(row)) * 16);
+    voff[i] = row * ROWB + ((pc ^ v_swizzle<D>(row)) * 16);
+  }
+  auto issue = [&](const __amdgpu_buffer_rsrc_t& r, uint16_t* dst, const int (&off)[IPW], int j) {
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int u = tid + kThreads * i, quad = u / CPR, ch = u % CPR;
-      if (u >= VUN) break;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = key0 + 4 * quad + r;
-        vpre[i][r] = key < N ? *reinterpret_cast<const u32x4*>(Vg + (size_t)key * D + ch * 8) : u32x4{0, 0, 0, 0};
-      }
-    }
+    for (int i = 0; i < IPW; ++i)
+      lds_dma16(r, dst + (wave * IPW + i) * 512, off[i] + j * BC * ROWB);
   };
 
-  auto store_tile = [&](int buf) {
+  // ---- per-lane LDS read offsets (elements) --------------------------------
+  // K A-operand: row kb*32 + l32, chunk 2 st + hi (swizzled).
+  // V^T A-operand via the transposed read: within each 16-lane group, source
+  // lane s addresses row kbase + s/4, columns dbase + 4 (s%4) .. +3; lane i of
+  // the group then receives column dbase + i, rows kbase .. kbase + 3.
+  const int grp = lane >> 4, sl = lane & 15;
+  const int v_row_in = sl >> 2;                 // + kbase
+  const int v_col_in = 16 * (grp & 1) + 4 * (sl & 3);  // + 32 db
+
+  auto qk = [&](f32x16 (&s)[NKB], const uint16_t* ks) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int ci = tid + kThreads * i, row = ci / CPR, ch = ci % CPR;
-      *reinterpret_cast<u32x4*>(&Ks[buf][row * D + ((ch ^ k_swizzle<D>(row)) * 8)]) = kpre[i];
-    }
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int u = tid + kThreads * i, quad = u / CPR, ch = u % CPR;
-      if (u >= VUN) break;
-      // 4 keys x 8 d  ->  8 d x 4 keys; dword m of a key row holds d = 2m, 2m+1
-      u32x4* dst = reinterpret_cast<u32x4*>(&Vs[buf][(quad * D + ch * 8) * 4]);
+    for (int st = 0; st < NQS; ++st)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        u32x4 w;
-        w[0] = perm_b32(vpre[i][1][m], vpre[i][0][m], 0x05040100u);
-        w[1] = perm_b32(vpre[i][3][m], vpre[i][2][m], 0x05040100u);
-        w[2] = perm_b32(vpre[i][1][m], vpre[i][0][m], 0x07060302u);
-        w[3] = perm_b32(vpre[i][3][m], vpre[i][2][m], 0x07060302u);
-        dst[m] = w;
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int row = kb * 32 + l32;
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(&ks[row * D + (((2 * st + hi) ^ k_swizzle<D>(row)) * 8)]);
+        s[kb] = mfma_bf16_32x32x16(a, qreg[st], s[kb]);
       }
-    }
   };
 
-  float m_run = -INFINITY;  // running max of the raw scores of row qrow
+  auto read_vt = [&](const uint16_t* vs, int kbase, int db) -> i16x4 {
+    const int row = kbase + v_row_in;
+    const int col = 32 * db + v_col_in;
+    const int e = row * D + (((col >> 3) ^ v_swizzle<D>(row)) << 3) + (col & 7);
+    return lds_read_tr16(&vs[e]);
+  };
+
+  float m_run = -INFINITY;  // exponent reference of row qrow (raw score units)
   float l_run = 0.f;        // this half-wave's share of the running sum
   f32x16 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
-
   const float c = p.c;
+  const float lazy = kLazyLog2 / c;  // the same threshold in raw score units
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    const bool more = j + 1 < ntiles;
+  // one step for tile j: softmax of S_j (s_in), S_{j+1} into s_out,
+  // O += V_j^T P_j^T; the ring slots are passed as compile-time LDS objects:
+  //   k_this: holds K_j until this step, then receives K_{j+2};  k_next: K_{j+1}
+  //   v_this: V_j;  v_next: receives V_{j+1}
+  auto step = [&](int j, f32x16 (&s_in)[NKB], f32x16 (&s_out)[NKB], uint16_t* k_this, const uint16_t* k_next,
+                  const uint16_t* v_this, uint16_t* v_next) {
+    wait_vmem_all();
+    __syncthreads();  // V_j and K_{j+1} are in LDS; every wave is done with K_j and V_{j-1}
+    if (j + 2 < ntiles) issue(rk, k_this, koff, j + 2);
+    if (j + 1 < ntiles) issue(rv, v_next, voff, j + 1);
     const int key0 = j * BC;
     const bool active = !CAUSAL || key0 <= q0 + kQW - 1;
-    if (!active && more) load_tile(j + 1);
-    if (active) {
-      // ---- S^T = K_j Q^T ------------------------------------------------
-      f32x16 s[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        s[kb] = f32x16{};
-        const int row = kb * 32 + l32;
-        const uint16_t* krow = &Ks[buf][row * D];
-        const int sw = k_swizzle<D>(row);
-#pragma unroll
-        for (int st = 0; st < NQS; ++st) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + (((2 * st + hi) ^ sw) * 8));
-          s[kb] = mfma_bf16_32x32x16(a, qreg[st], s[kb]);
-        }
-      }
-      // ---- mask (only tiles crossing the diagonal or the end of N) ------
-      const bool need_mask = (CAUSAL && key0 + BC - 1 > q0) || (key0 + BC > N);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const bool dead = (CAUSAL && key > qrow) || key >= N;
-            s[kb][r] = dead ? -INFINITY : s[kb][r];
-          }
-      }
-      // ---- online softmax in the exp2 domain ------------------------------
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmax3(mx, s[kb][r], s[kb][r + 1]);
-      mx = __builtin_fmaxf(mx, swap_halves(mx));
-      const float m_new = __builtin_fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float mc = m_use * c;
-      const float alpha = exp2_fast(m_run * c - mc);
-      float lsum = 0.f;
+    if (!active) return;  // causal: every row of this wave lies above tile j (and all later ones)
+
+    // ---- mask (only tiles crossing the diagonal or the end of N) ----------
+    const bool need_mask = (CAUSAL && key0 + BC - 1 > q0) || (key0 + BC > N);
+    if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = exp2_fast(__builtin_fmaf(s[kb][r], c, -mc));
-          s[kb][r] = e;
-          lsum += e;
+          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const bool dead = (CAUSAL && key > qrow) || key >= N;
+          s_in[kb][r] = dead ? -INFINITY : s_in[kb][r];
         }
-      l_run = alpha * l_run + lsum;
-      m_run = m_new;
+    }
+    // ---- row max and the lazy rescale decision --------------------------------
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmax3(mx, s_in[kb][r], s_in[kb][r + 1]);
+    mx = __builtin_fmaxf(mx, swap_halves(mx));
+    if (__any(mx > m_run + lazy)) {
+      const float m_new = __builtin_fmaxf(m_run, mx);
+      const float alpha = exp2_fast((m_run - m_new) * c);  // 0 on the first tile
+      l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-      // P^T as bf16 B operands: k-step ks uses registers 8t..8t+7 of block ks/2
-      bf16x8 pb[NPS];
+      m_run = m_new;
+    }
+    const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+
+    // ---- one branch-free block: S_{j+1} = K_{j+1} Q^T on the matrix cores
+    // while exp2 / bf16 cast / row sum of S_j run on the vector ALUs.  For the
+    // last tile the product reads a stale slot and is never used.
+    qk(s_out, k_next);
+    bf16x8 pb[NPS];
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};  // fp32 partial row sums (four short chains)
 #pragma unroll
-      for (int ks = 0; ks < NPS; ++ks) {
-        const int kb = ks >> 1, r0 = (ks & 1) * 8;
-        u32x4 t;
-        t[0] = pack_bf16x2(s[kb][r0 + 0], s[kb][r0 + 1]);
-        t[1] = pack_bf16x2(s[kb][r0 + 2], s[kb][r0 + 3]);
-        t[2] = pack_bf16x2(s[kb][r0 + 4], s[kb][r0 + 5]);
-        t[3] = pack_bf16x2(s[kb][r0 + 6], s[kb][r0 + 7]);
-        pb[ks] = __builtin_bit_cast(bf16x8, t);
+    for (int ks = 0; ks < NPS; ++ks) {
+      const int kb = ks >> 1, r0 = (ks & 1) * 8;
+      u32x4 t;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float e0 = exp2_fast(__builtin_fmaf(s_in[kb][r0 + 2 * h], c, -mc));
+        const float e1 = exp2_fast(__builtin_fmaf(s_in[kb][r0 + 2 * h + 1], c, -mc));
+        t[h] = pack_bf16x2(e0, e1);
+        ls[h] += e0 + e1;
       }
-      // next tile's global loads fly while the PV products run
-      if (more) load_tile(j + 1);
-      // ---- O^T += V_j^T P^T -----------------------------------------------
-      // k-step ks covers keys 16ks + 4hi + 0..3 and 16ks + 8 + 4hi + 0..3,
-      // i.e. key quads 4ks + hi and 4ks + 2 + hi.
+      pb[ks] = __builtin_bit_cast(bf16x8, t);
+    }
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    // ---- O^T += V_j^T P_j^T ---------------------------------------------------
+    // k-step ks covers keys 16ks + 4hi + 0..3 (first read) and 16ks + 8 + 4hi
+    // + 0..3 (second read): the key order of the P^T registers.
+#pragma unroll
+    for (int ks = 0; ks < NPS; ++ks)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int dcol = db * 32 + l32;
-#pragma unroll
-        for (int ks = 0; ks < NPS; ++ks) {
-          const u32x2 a0 = *reinterpret_cast<const u32x2*>(&Vs[buf][((4 * ks + hi) * D + dcol) * 4]);
-          const u32x2 a1 = *reinterpret_cast<const u32x2*>(&Vs[buf][((4 * ks + 2 + hi) * D + dcol) * 4]);
-          const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
-          o[db] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, a), pb[ks], o[db]);
-        }
+        const i16x4 a0 = read_vt(v_this, 16 * ks + 4 * hi, db);
+        const i16x4 a1 = read_vt(v_this, 16 * ks + 8 + 4 * hi, db);
+        const u32x2 w0 = __builtin_bit_cast(u32x2, a0), w1 = __builtin_bit_cast(u32x2, a1);
+        const u32x4 a = {w0[0], w0[1], w1[0], w1[1]};
+        o[db] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, a), pb[ks], o[db]);
       }
-    }
-    if (more) store_tile(buf ^ 1);
-    __syncthreads();
+  };
+
+  // ---- prologue: K_0, V_0, K_1 in flight; S_0 -----------------------------
+  f32x16 sa[NKB], sb[NKB];
+  issue(rk, Ks0, koff, 0);
+  issue(rv, Vs0, voff, 0);
+  if (ntiles > 1) issue(rk, Ks1, koff, 1);
+  wait_vmem_all();
+  __syncthreads();
+  qk(sa, Ks0);
+  for (int j = 0; j < ntiles; j += 2) {
+    step(j, sa, sb, Ks0, Ks1, Vs0, Vs1);
+    if (j + 1 < ntiles) step(j + 1, sb, sa, Ks1, Ks0, Vs1, Vs0);
   }
 
   // ---- epilogue: O / l, lse = m * scale + ln l ----------------------------

@@ -46,7 +46,7 @@ extern "C" {
 enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL_PTR = -1, /* a required pointer is NULL                              */
-  FA_ERR_SHAPE = -2,    /* B, H or N < 1, or an element count >= 2^40              */
+  FA_ERR_SHAPE = -2,    /* B, H or N < 1, >= 2^40 elements, or N * d * 2 >= 2^31   */
   FA_ERR_HEADDIM = -3,  /* d not supported by this entry point                     */
   FA_ERR_ARG = -4,      /* causal not 0/1, scale not finite and > 0, bad flags     */
   FA_ERR_ALIGN = -5,    /* a pointer is not 16-byte aligned                        */

@@ -53,7 +53,25 @@ __global__ void k_tr16(const int* addr, short* out) {
   for (int e = 0; e < 4; ++e) out[4 * l + e] = r[e];
 }
 
+// direct-to-LDS buffer load: lane l loads the 16 bytes at byte offset
+// off[l] of a buffer whose range is nbytes; LDS is then copied out (1 KB)
+__global__ void k_load_lds(const uint32_t* src, const int* off, int nbytes, uint32_t* out) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds[256 + 64];
+  const int l = threadIdx.x;
+  for (int i = l; i < 320; i += 64) lds[i] = 0xdeadbeefu;
+  __syncthreads();
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, nbytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds + 16), 16, off[l], 0, 0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int i = l; i < 320; i += 64) out[i] = lds[i];
+}
+
 extern "C" {
+int probe_load_lds(const uint32_t* src, const int* off, int nbytes, uint32_t* out, void* s) {
+  hipLaunchKernelGGL(k_load_lds, dim3(1), dim3(64), 0, (hipStream_t)s, src, off, nbytes, out);
+  return hipGetLastError();
+}
 int probe_mfma_bf16(const void* a, const void* b, float* c, void* s) {
   hipLaunchKernelGGL(k_mfma_bf16, dim3(1), dim3(64), 0, (hipStream_t)s, (const bf16x8*)a, (const bf16x8*)b, (f32x16*)c);
   return hipGetLastError();

@@ -21,7 +21,7 @@ def probes():
         pytest.fail("GPU test collected on a machine without a GPU")
     lib = ctypes.CDLL(LIB)
     for n in ("probe_mfma_bf16", "probe_mfma_fp8", "probe_mfma_fp8_unscaled", "probe_cvt_fp8", "probe_swap_halves",
-              "probe_tr16"):
+              "probe_tr16", "probe_load_lds"):
         getattr(lib, n).restype = ctypes.c_int
     return lib
 
@@ -139,3 +139,23 @@ def test_ds_read_tr16_b64_mapping(probes):
             f.write(f"{l}: {list(map(int, o[l]))}\n")
     print("tr16 lane 0..3:", o[:4].tolist())
     assert o.min() >= 0 and o.max() < 256
+
+
+def test_buffer_load_lds_placement_and_range(probes):
+    # lane l loads 16 bytes from a permuted offset; they land at LDS base
+    # + 16 l; offsets at or past the buffer's range read as zero
+    src = torch.arange(512, dtype=torch.int32, device="cuda")  # 2 KB of distinct words
+    perm = np.random.default_rng(0).permutation(64)
+    off = (perm * 16).astype(np.int32)
+    off[60:] = [1024, 1040, 2048, 4096]  # beyond nbytes = 1024: zero
+    out = torch.zeros(320, dtype=torch.int32, device="cuda")
+    assert probes.probe_load_lds(_p(src), _p(torch.from_numpy(off).cuda()), 1024, _p(out), _s()) == 0
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().view(np.uint32)
+    assert np.all(o[:16] == 0xDEADBEEF) and np.all(o[16 + 256:] == 0xDEADBEEF)
+    got = o[16:16 + 256].reshape(64, 4)
+    for l in range(64):
+        if l < 60:
+            np.testing.assert_array_equal(got[l], np.arange(4) + perm[l] * 4)
+        else:
+            np.testing.assert_array_equal(got[l], 0)
