@@ -17,9 +17,12 @@
 // fused into a pass that happens anyway instead of costing its own HBM
 // round trip).
 //
-// Forward: same decomposition and online softmax as the bf16 kernel (one
-// workgroup of 4 waves per 128 query rows, S^T = K Q^T and O^T = V^T P^T on
-// v_mfma_f32_32x32x64_f8f6f4, fp32 accumulation and softmax state).  Scores
+// Forward: same decomposition, data path and online softmax as the bf16
+// kernel (one workgroup of 4 waves per 128 query rows, direct-to-LDS K and
+// V^T rings with K one tile ahead, S^T = K Q^T and O^T = V^T P^T on
+// v_mfma_f32_32x32x64_f8f6f4 with fp32 accumulation and softmax state); the
+// running max is exact (the rescale is skipped only when no row grew), so
+// the probabilities stay in (0, 1].  Scores
 // are descaled by folding s_Q,i * s_K,j into the exp2 constant of each
 // tile; probabilities are produced directly as P * 2^7 * mu_j (exp2 bias)
 // and cast to E4M3, and the PV instruction's block exponents supply
@@ -162,12 +165,23 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8PrepParams p) {
       *reinterpret_cast<u32x2*>(&tr[lr * 8 + e][grp * 8]) = w;
     }
     __syncthreads();
-    // row d of the block: 128 bytes = 8 x 16 B; 256 threads write 2 chunks each
+    // Row d of the block: 128 keys = two 64-key segments of 16 four-key
+    // groups each.  Within a segment, word w of the output holds key group
+    // 2 (w % 8) + w / 8 (even groups first, then odd groups): the order in
+    // which a lane of the forward kernel's PV product takes its keys.
     uint8_t* Y = p.x8 + (size_t)bh * D * p.ld;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ci = tid + 256 * i, d = ci >> 3, ch = ci & 7;
-      *reinterpret_cast<u32x4*>(Y + (size_t)d * p.ld + n0 + ch * 16) = *reinterpret_cast<const u32x4*>(&tr[d][ch * 16]);
+      const int seg = ch >> 2, w0 = (ch & 3) * 4;
+      const uint32_t* row = reinterpret_cast<const uint32_t*>(&tr[d][0]);
+      u32x4 v;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int w = w0 + t;
+        v[t] = row[16 * seg + 2 * (w & 7) + (w >> 3)];
+      }
+      *reinterpret_cast<u32x4*>(Y + (size_t)d * p.ld + n0 + ch * 16) = v;
     }
   }
 }
@@ -202,22 +216,42 @@ constexpr int kWaves = 4;
 constexpr int kQW = 32;
 constexpr int kBR = kWaves * kQW;  // 128 = one scale block of queries
 constexpr int kBC = 64;            // keys per tile (half a scale block)
-constexpr int kThreads = 256;
+constexpr int kThreads = kWaves * 64;
 
-// 16-byte chunk swizzles (see the bf16 kernel): K rows are 128 bytes, V^T
-// tile rows are 64 bytes.
+typedef __attribute__((address_space(3))) void* lds_void_t;
+
+// vmcnt(0), expcnt and lgkmcnt left open; as a builtin the compiler knows the
+// vector-memory counter is empty afterwards and adds no waits of its own
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// 16 bytes per lane from buffer offset voff straight into LDS at dst + 16 * lane
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint8_t* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t)dst, 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// 16-byte chunk swizzles: K rows are 128 bytes (two rows per 256 bytes of
+// banks), V^T tile rows are 64 bytes (four rows per 256 bytes).
 __device__ __forceinline__ int k8_swizzle(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int v8_swizzle(int d) { return (d >> 2) & 3; }
 
 template <bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
   constexpr int D = 128;
-  constexpr int NKB = kBC / 32;  // 2
+  constexpr int NKB = kBC / 32;  // 2 key blocks of S^T per tile
   constexpr int NDB = D / 32;    // 4
   constexpr int NQS = D / 64;    // 2 k-steps of 64 d
+  constexpr int TILE = kBC * D;  // bytes of a K tile (and of a V^T tile)
+  constexpr int IPW = TILE / 1024 / kWaves;  // 1 KB wave-loads per wave per tile (2)
 
-  __shared__ __attribute__((aligned(16))) uint8_t Ks[2][kBC * D];  // [key][d], swizzled
-  __shared__ __attribute__((aligned(16))) uint8_t Vs[2][D * kBC];  // [d][64 keys], permuted + swizzled
+  // one LDS object per ring slot (compile-time slots: see the bf16 kernel)
+  __shared__ __attribute__((aligned(1024))) uint8_t Ks0[TILE];  // [key][d], swizzled
+  __shared__ __attribute__((aligned(1024))) uint8_t Ks1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vs0[TILE];  // [d][64 keys], swizzled
+  __shared__ __attribute__((aligned(1024))) uint8_t Vs1[TILE];
 
   const int N = p.N;
   const int BH = p.B * p.H;
@@ -236,8 +270,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const uint8_t* __restrict__ Qg = p.q8 + (size_t)bh * N * D;
-  const uint8_t* __restrict__ Kg = p.k8 + (size_t)bh * N * D;
-  const uint8_t* __restrict__ Vg = p.v8t + (size_t)bh * D * p.ld;
   const float* __restrict__ ks = p.ks + (size_t)bh * nb;
   const float* __restrict__ vs = p.vs + (size_t)bh * nb;
   const int q0 = qt * kBR + wave * kQW;
@@ -260,138 +292,152 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
   const int kend = CAUSAL ? min(N, qt * kBR + kBR) : N;
   const int ntiles = (kend + kBC - 1) / kBC;
 
-  // K tile: 64 rows x 8 chunks = 512 chunks, 2 per thread.
-  // V^T tile: 128 rows (d) x 64 keys = 2 halves of 32 bytes per row, one
-  // half per thread; dword i of the row moves to (i & 1) * 8 + (i >> 1).
-  u32x4 kpre[2];
-  u32x4 vpre[2];
-  auto load_tile = [&](int j) {
-    const int key0 = j * kBC;
+  // ---- direct-to-LDS loads -------------------------------------------------
+  // K: wave-load i of wave w fills 8 rows of 128 bytes; lane L writes
+  // physical chunk L % 8 of row L / 8.  V^T: wave-load i fills 16 rows (d) of
+  // 64 bytes (the tile's keys of that row); lane L writes physical chunk
+  // L % 4 of row L / 4.  Each lane fetches the logical chunk the swizzle
+  // puts there.  The V^T rows arrive already in the PV operand's key order.
+  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(p.k8 + (size_t)bh * N * D, N * D);
+  const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(p.v8t + (size_t)bh * D * p.ld, D * p.ld);
+  int koff[IPW], voff[IPW];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ci = tid + kThreads * i, row = ci >> 3, ch = ci & 7, key = key0 + row;
-      kpre[i] = key < N ? *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + ch * 16) : u32x4{0, 0, 0, 0};
-    }
-    const int d = tid >> 1, half = tid & 1;
-    const u32x4* src = reinterpret_cast<const u32x4*>(Vg + (size_t)d * p.ld + key0 + half * 32);
-    vpre[0] = src[0];  // padded to a multiple of 128 columns: always in bounds
-    vpre[1] = src[1];
+  for (int i = 0; i < IPW; ++i) {
+    const int ins = wave * IPW + i;
+    const int kr = ins * 8 + (lane >> 3), kc = lane & 7;
+    koff[i] = kr * D + ((kc ^ k8_swizzle(kr)) * 16);
+    const int vd = ins * 16 + (lane >> 2), vc = lane & 3;
+    voff[i] = vd * p.ld + ((vc ^ v8_swizzle(vd)) * 16);
+  }
+  auto issue_k = [&](uint8_t* dst, int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) lds_dma16(rk, dst + (wave * IPW + i) * 1024, koff[i] + j * kBC * D);
   };
-  auto store_tile = [&](int buf) {
+  auto issue_v = [&](uint8_t* dst, int j) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ci = tid + kThreads * i, row = ci >> 3, ch = ci & 7;
-      *reinterpret_cast<u32x4*>(&Ks[buf][row * D + ((ch ^ k8_swizzle(row)) * 16)]) = kpre[i];
-    }
-    const int d = tid >> 1, half = tid & 1;
-    // dwords 16 half + {0, 2, 4, 6} -> slot half (chunk half), {1, 3, 5, 7} -> chunk 2 + half
-    const u32x4 ev = {vpre[0][0], vpre[0][2], vpre[1][0], vpre[1][2]};
-    const u32x4 od = {vpre[0][1], vpre[0][3], vpre[1][1], vpre[1][3]};
-    uint8_t* row = &Vs[buf][d * kBC];
-    *reinterpret_cast<u32x4*>(row + ((half ^ v8_swizzle(d)) * 16)) = ev;
-    *reinterpret_cast<u32x4*>(row + (((2 + half) ^ v8_swizzle(d)) * 16)) = od;
+    for (int i = 0; i < IPW; ++i) lds_dma16(rv, dst + (wave * IPW + i) * 1024, voff[i] + j * kBC);
   };
 
+  auto qk = [&](f32x16 (&s)[NKB], const uint8_t* kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < NQS; ++st)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int row = kb * 32 + l32;
+        const uint8_t* krow = kt + row * D;
+        const int sw = k8_swizzle(row);
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(krow + (((4 * st + 2 * hi) ^ sw) * 16));
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(krow + (((4 * st + 2 * hi + 1) ^ sw) * 16));
+        const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                         (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        s[kb] = mfma_fp8_32x32x64(a, qreg[st], s[kb], 127, 127);
+      }
+  };
+
+  float ks_next = 0.f, vs_next = 0.f;  // K and V scales of the next tile to process
   float m_run = -INFINITY;  // running max of the log2-domain scores of row qrow
   float l_run = 0.f;
   f32x16 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) load_tile(j + 1);
+  // one step for tile j: softmax of S_j (s_in), S_{j+1} into s_out,
+  // O += V_j^T P_j^T; ring slots as in the bf16 kernel.
+  auto step = [&](int j, f32x16 (&s_in)[NKB], f32x16 (&s_out)[NKB], uint8_t* k_this, const uint8_t* k_next,
+                  const uint8_t* v_this, uint8_t* v_next) __attribute__((always_inline)) {
     const int key0 = j * kBC;
-    const bool active = !CAUSAL || key0 <= q0 + kQW - 1;
-    if (active) {
-      const int sb = key0 >> 7;  // scale block of this key tile
-      const float ct = cq * ks[sb];
-      const float sv = vs[sb];
-      const uint32_t svb = __float_as_uint(sv);
-      const int v_exp = (int)((svb >> 23) & 0xffu);                   // E8M0 block exponent of s_V
-      const float mu = __uint_as_float((svb & 0x007fffffu) | 0x3f800000u);  // s_V mantissa in [1, 2)
-      const float pbias = 7.f + __builtin_amdgcn_logf(mu);           // log2(2^7 mu)
-      const float inv_f = 1.f / (128.f * mu);
+    wait_vmem_all();
+    __syncthreads();
+    // the scales of tile j arrived with the previous step's loads; fetch
+    // those of tile j + 1 behind this step's DMAs
+    const float ksc = ks_next, vsc = vs_next;
+    if (j + 2 < ntiles) issue_k(k_this, j + 2);
+    if (j + 1 < ntiles) {
+      issue_v(v_next, j + 1);
+      ks_next = ks[(key0 + kBC) >> 7];
+      vs_next = vs[(key0 + kBC) >> 7];
+    }
+    if (CAUSAL && key0 > q0 + kQW - 1) return;
 
-      f32x16 s[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        s[kb] = f32x16{};
-        const int row = kb * 32 + l32;
-        const uint8_t* krow = &Ks[buf][row * D];
-        const int sw = k8_swizzle(row);
-#pragma unroll
-        for (int st = 0; st < NQS; ++st) {
-          const u32x4 a0 = *reinterpret_cast<const u32x4*>(krow + (((4 * st + 2 * hi) ^ sw) * 16));
-          const u32x4 a1 = *reinterpret_cast<const u32x4*>(krow + (((4 * st + 2 * hi + 1) ^ sw) * 16));
-          const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2],
-                           (int)a1[3]};
-          s[kb] = mfma_fp8_32x32x64(a, qreg[st], s[kb], 127, 127);
-        }
-      }
-      const bool need_mask = (CAUSAL && key0 + kBC - 1 > q0) || (key0 + kBC > N);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const bool dead = (CAUSAL && key > qrow) || key >= N;
-            s[kb][r] = dead ? -INFINITY : s[kb][r];
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmax3(mx, s[kb][r], s[kb][r + 1]);
-      mx = __builtin_fmaxf(mx, swap_halves(mx)) * ct;  // ct > 0; -inf stays -inf
-      const float m_new = __builtin_fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run - m_use);
-      const float moff = m_use - pbias;
-      float lsum = 0.f;
+    const float ct = cq * ksc;
+    const uint32_t svb = __float_as_uint(vsc);
+    const int v_exp = (int)((svb >> 23) & 0xffu);                          // E8M0 exponent of s_V
+    const float mu = __uint_as_float((svb & 0x007fffffu) | 0x3f800000u);  // s_V mantissa in [1, 2)
+    const float pbias = 7.f + __builtin_amdgcn_logf(mu);                  // log2(2^7 mu); 7 for power-of-two s_V
+    const float inv_f = 1.f / (128.f * mu);
+
+    const bool need_mask = (CAUSAL && key0 + kBC - 1 > q0) || (key0 + kBC > N);
+    if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = exp2_fast(__builtin_fmaf(s[kb][r], ct, -moff));  // P * 2^7 * mu
-          s[kb][r] = e;
-          lsum += e;
+          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const bool dead = (CAUSAL && key > qrow) || key >= N;
+          s_in[kb][r] = dead ? -INFINITY : s_in[kb][r];
         }
-      l_run = alpha * l_run + lsum * inv_f;
-      m_run = m_new;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmax3(mx, s_in[kb][r], s_in[kb][r + 1]);
+    mx = __builtin_fmaxf(mx, swap_halves(mx)) * ct;  // ct > 0; -inf stays -inf
+    // the exact running max (probabilities stay in (0, 1]); skip the rescale
+    // when no row of the wave grew, where every alpha would be exactly 1
+    if (__any(mx > m_run)) {
+      const float m_new = __builtin_fmaxf(m_run, mx);
+      const float alpha = exp2_fast(m_run - m_new);  // 0 on the first tile
+      l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-      // P^T operand: byte 4w + t of the lane = register 4(w%4) + t of block w/4
-      i32x8 pb;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const int kb = w >> 2, r = 4 * (w & 3);
-        pb[w] = (int)cvt_e4m3x4(s[kb][r], s[kb][r + 1], s[kb][r + 2], s[kb][r + 3]);
-      }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int d = db * 32 + l32;
-        const uint8_t* vrow = &Vs[buf][d * kBC];
-        const int sw = v8_swizzle(d);
-        // slot order in the row: chunk 0 = even dwords of half 0, 1 = even of
-        // half 1, 2 = odd of half 0, 3 = odd of half 1; lane half hi needs the
-        // keys 8w + 4hi .. +3 (w = 0..7) = dword 2w + hi of the 64-key row,
-        // which are exactly chunks 2hi and 2hi + 1 in order.
-        const u32x4 c0 = *reinterpret_cast<const u32x4*>(vrow + (((2 * hi) ^ sw) * 16));
-        const u32x4 c1 = *reinterpret_cast<const u32x4*>(vrow + (((2 * hi + 1) ^ sw) * 16));
-        const i32x8 a = {(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], (int)c1[0], (int)c1[1], (int)c1[2],
-                         (int)c1[3]};
-        o[db] = mfma_fp8_32x32x64(a, pb, o[db], v_exp, 127 - 7);
-      }
+      m_run = m_new;
     }
-    if (j + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
+    const float moff = ((m_run == -INFINITY) ? 0.f : m_run) - pbias;
+
+    qk(s_out, k_next);  // S_{j+1}: matrix cores, while the exps below run
+    i32x8 pb;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int kb = w >> 2, r = 4 * (w & 3);
+      const float e0 = exp2_fast(__builtin_fmaf(s_in[kb][r], ct, -moff));  // P * 2^7 * mu
+      const float e1 = exp2_fast(__builtin_fmaf(s_in[kb][r + 1], ct, -moff));
+      const float e2 = exp2_fast(__builtin_fmaf(s_in[kb][r + 2], ct, -moff));
+      const float e3 = exp2_fast(__builtin_fmaf(s_in[kb][r + 3], ct, -moff));
+      ls[w & 3] += (e0 + e1) + (e2 + e3);
+      pb[w] = (int)cvt_e4m3x4(e0, e1, e2, e3);
+    }
+    l_run += ((ls[0] + ls[1]) + (ls[2] + ls[3])) * inv_f;
+    // O^T += V^T P^T: lane half hi reads the 32 bytes [32 hi, 32 hi + 32) of
+    // row d, which hold keys 8w + 4hi .. +3 for w = 0..7 (the prep's order)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = db * 32 + l32;
+      const uint8_t* vrow = v_this + d * kBC;
+      const int sw = v8_swizzle(d);
+      const u32x4 c0 = *reinterpret_cast<const u32x4*>(vrow + (((2 * hi) ^ sw) * 16));
+      const u32x4 c1 = *reinterpret_cast<const u32x4*>(vrow + (((2 * hi + 1) ^ sw) * 16));
+      const i32x8 a = {(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3],
+                       (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
+      o[db] = mfma_fp8_32x32x64(a, pb, o[db], v_exp, 127 - 7);
+    }
+  };
+
+  f32x16 sa[NKB], sb[NKB];
+  issue_k(Ks0, 0);
+  issue_v(Vs0, 0);
+  ks_next = ks[0];
+  vs_next = vs[0];
+  if (ntiles > 1) issue_k(Ks1, 1);
+  wait_vmem_all();
+  __syncthreads();
+  qk(sa, Ks0);
+  for (int j = 0; j < ntiles; j += 2) {
+    step(j, sa, sb, Ks0, Ks1, Vs0, Vs1);
+    if (j + 1 < ntiles) step(j + 1, sb, sa, Ks1, Ks0, Vs1, Vs0);
   }
 
   const float l_tot = l_run + swap_halves(l_run);

@@ -8,9 +8,13 @@
 // ever exists as 32 x 32 register tiles.
 //
 // Work decomposition (FA3 explainer, section "FA2 到 H100 后，瓶颈为什么又变了":
-// parallelism over batch, heads and query tiles): one workgroup of 4 waves
-// per (batch, head, 128-row query tile); each wave owns 32 query rows; two
-// workgroups share a CU, so every SIMD interleaves two waves.
+// parallelism over batch, heads and query tiles): one workgroup of NW waves
+// per (batch, head, NW * 32 QB query rows); each wave owns QB blocks of 32
+// query rows, so every K or V operand read from LDS feeds QB matrix
+// instructions (LDS read bandwidth, not the matrix cores, is what 32 rows
+// per wave runs into).  With QB = 2 a wave needs more than 256 registers
+// and runs alone on its SIMD, so the overlap of matrix and vector work is
+// built into each wave's own instruction stream.
 //
 // Per wave the products are computed transposed, S^T = K Q^T and
 // O^T = V^T P^T, so that a lane owns ONE query row (column L & 31 of every
@@ -30,7 +34,8 @@
 // step for tile j the workgroup holds K_{j+1} and V_j, and the loads of
 // K_{j+2} and V_{j+1} are in flight, in 2-slot rings (slot = tile mod 2).
 // Inside a wave, S_{j+1} = K_{j+1} Q^T is issued on the matrix cores while
-// the softmax of S_j runs on the vector ALUs (two S buffers, S_cur/S_next).
+// the softmax of S_j runs on the vector ALUs (two S buffers, S_cur/S_next),
+// and the row max of S_{j+1} is taken while O += V_j^T P_j^T runs.
 // Q stays in VGPRs for the whole loop.  K is stored row-major with an XOR
 // swizzle of 16-byte chunks (conflict-free A-operand reads); V is stored
 // row-major with its own swizzle and read transposed with ds_read_b64_tr_b16.
@@ -51,16 +56,25 @@
 namespace fa {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kQW = 32;              // query rows per wave
-constexpr int kBR = kWaves * kQW;    // query rows per workgroup
-constexpr int kThreads = kWaves * 64;
-constexpr float kLazyLog2 = 8.f;     // rescale only when a row max grows by more than 2^8
+constexpr float kLazyLog2 = 8.f;  // rescale only when a row max grows by more than 2^8
 
+// Per head size: QB 32-row query blocks per wave, NW waves per workgroup,
+// BC keys per tile, MINB workgroups per CU.  Measured on MI355X: one query
+// block per wave with two workgroups per CU (two waves per SIMD that
+// interleave on the matrix cores) beats two blocks per wave at one wave per
+// SIMD, which halves the LDS and L2 traffic per product but leaves a single
+// wave unable to hide its own latencies.
 template <int D> struct Bf16Cfg;
-template <> struct Bf16Cfg<64> { static constexpr int BC = 64; static constexpr int MINB = 2; };
-template <> struct Bf16Cfg<128> { static constexpr int BC = 64; static constexpr int MINB = 2; };
-template <> struct Bf16Cfg<256> { static constexpr int BC = 32; static constexpr int MINB = 1; };
+template <> struct Bf16Cfg<64> {
+  static constexpr int QB = 1, NW = 4, BC = 64, MINB = 2;
+};
+template <> struct Bf16Cfg<128> {
+  static constexpr int QB = 1, NW = 4, BC = 64, MINB = 2;
+};
+template <> struct Bf16Cfg<256> {
+  static constexpr int QB = 1, NW = 4, BC = 32, MINB = 1;
+};
+template <int D> constexpr int rows_per_workgroup() { return Bf16Cfg<D>::NW * 32 * Bf16Cfg<D>::QB; }
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -95,19 +109,69 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* src) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t)src);
 }
 
+// Instruction-group order for one pipeline step (compiler scheduling hints;
+// masks: 0x008 matrix, 0x100 LDS read, 0x002 vector ALU).  QK phase: each
+// K operand read feeds QB products and runs FA_KLEAD reads ahead, with VPM
+// softmax vector instructions between products; PV phase: each pair of
+// transposed V reads feeds QB products and runs one pair ahead, with the
+// row-max work of the next tile in between.
+#ifndef FA_SCHED
+#define FA_SCHED 1
+#endif
+#ifndef FA_KLEAD
+#define FA_KLEAD 2
+#endif
+#ifndef FA_VLEAD
+#define FA_VLEAD 4
+#endif
+#ifndef FA_VPM
+#define FA_VPM 5
+#endif
+#ifndef FA_VPP
+#define FA_VPP 2
+#endif
+template <int NKR, int NVR, int QB>
+__device__ __forceinline__ void schedule_step() {
+  if constexpr (FA_SCHED) {
+    __builtin_amdgcn_sched_group_barrier(0x100, FA_KLEAD, 0);
+#pragma unroll
+    for (int i = 0; i < NKR; ++i) {
+#pragma unroll
+      for (int q = 0; q < QB; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, FA_VPM, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, FA_VLEAD, 0);
+#pragma unroll
+    for (int i = 0; i < NVR; ++i) {
+#pragma unroll
+      for (int q = 0; q < QB; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, FA_VPP, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  }
+}
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, Bf16Cfg<D>::MINB) void fwd_bf16_kernel(FwdBf16Params p) {
-  constexpr int BC = Bf16Cfg<D>::BC;
+__global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, Bf16Cfg<D>::MINB) void fwd_bf16_kernel(FwdBf16Params p) {
+  using Cfg = Bf16Cfg<D>;
+  constexpr int QB = Cfg::QB, NW = Cfg::NW, BC = Cfg::BC;
+  constexpr int QW = 32 * QB;                 // query rows per wave
+  constexpr int BR = NW * QW;                 // query rows per workgroup
   constexpr int ROWB = D * 2;                 // bytes per K/V row
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
   constexpr int INSTR = BC * ROWB / 1024;     // 1 KB wave-loads per tile
-  constexpr int IPW = INSTR / kWaves;         // ... per wave
+  constexpr int IPW = INSTR / NW;             // ... per wave
   constexpr int RPI = 1024 / ROWB;            // rows per wave-load
   constexpr int NKB = BC / 32;                // 32-key blocks of S^T per tile
   constexpr int NDB = D / 32;                 // 32-row blocks of O^T
   constexpr int NQS = D / 16;                 // k-steps of S^T = K Q^T
   constexpr int NPS = BC / 16;                // k-steps of O^T = V^T P^T
-  static_assert(INSTR % kWaves == 0, "tile must split over the waves");
+  static_assert(INSTR % NW == 0, "tile must split over the waves");
 
   // one LDS object per ring slot, addressed with compile-time slot numbers,
   // so the compiler can tell the slot being filled from the slots being read
@@ -118,7 +182,7 @@ __global__ __launch_bounds__(kThreads, Bf16Cfg<D>::MINB) void fwd_bf16_kernel(Fw
 
   const int N = p.N;
   const int BH = p.B * p.H;
-  const int nq = (N + kBR - 1) / kBR;
+  const int nq = (N + BR - 1) / BR;
   int bh, qt;
   if constexpr (CAUSAL) {
     // heaviest query tiles first; heads vary fastest so every XCD gets a mix
@@ -133,23 +197,26 @@ __global__ __launch_bounds__(kThreads, Bf16Cfg<D>::MINB) void fwd_bf16_kernel(Fw
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const size_t base = (size_t)bh * N * D;
-  const int q0 = qt * kBR + wave * kQW;  // first query row of this wave
-  const int qrow = q0 + l32;             // the query row this lane owns
+  const int q0 = qt * BR + wave * QW;  // first query row of this wave
+  int qrow[QB];                        // the query rows this lane owns
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) qrow[qb] = q0 + 32 * qb + l32;
 
-  // Q^T as the B operand, resident for the whole loop: k-step s holds
-  // d = 16 s + 8 hi .. +7 of row qrow.
-  bf16x8 qreg[NQS];
-  {
-    const bool ok = qrow < N;
-    const u32x4* src = reinterpret_cast<const u32x4*>(p.q + base + (size_t)(ok ? qrow : 0) * D);
+  // Q^T as B operands, resident for the whole loop: block qb, k-step s holds
+  // d = 16 s + 8 hi .. +7 of row qrow[qb].
+  bf16x8 qreg[QB][NQS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const bool ok = qrow[qb] < N;
+    const u32x4* src = reinterpret_cast<const u32x4*>(p.q + base + (size_t)(ok ? qrow[qb] : 0) * D);
 #pragma unroll
     for (int s = 0; s < NQS; ++s) {
       const u32x4 t = ok ? src[2 * s + hi] : u32x4{0, 0, 0, 0};
-      qreg[s] = __builtin_bit_cast(bf16x8, t);
+      qreg[qb][s] = __builtin_bit_cast(bf16x8, t);
     }
   }
 
-  const int kend = CAUSAL ? min(N, qt * kBR + kBR) : N;
+  const int kend = CAUSAL ? min(N, qt * BR + BR) : N;
   const int ntiles = (kend + BC - 1) / BC;
 
   // ---- direct-to-LDS tile loads -------------------------------------------
@@ -167,22 +234,15 @@ __global__ __launch_bounds__(kThreads, Bf16Cfg<D>::MINB) void fwd_bf16_kernel(Fw
   }
   auto issue = [&](const __amdgpu_buffer_rsrc_t& r, uint16_t* dst, const int (&off)[IPW], int j) {
 #pragma unroll
-    for (int i = 0; i < IPW; ++i)
-      lds_dma16(r, dst + (wave * IPW + i) * 512, off[i] + j * BC * ROWB);
+    for (int i = 0; i < IPW; ++i) lds_dma16(r, dst + (wave * IPW + i) * 512, off[i] + j * BC * ROWB);
   };
 
-  // ---- per-lane LDS read offsets (elements) --------------------------------
-  // K A-operand: row kb*32 + l32, chunk 2 st + hi (swizzled).
-  // V^T A-operand via the transposed read: within each 16-lane group, source
-  // lane s addresses row kbase + s/4, columns dbase + 4 (s%4) .. +3; lane i of
-  // the group then receives column dbase + i, rows kbase .. kbase + 3.
-  const int grp = lane >> 4, sl = lane & 15;
-  const int v_row_in = sl >> 2;                 // + kbase
-  const int v_col_in = 16 * (grp & 1) + 4 * (sl & 3);  // + 32 db
-
-  auto qk = [&](f32x16 (&s)[NKB], const uint16_t* ks) {
+  // S^T = K Q^T: each K operand (row kb*32 + l32, chunk 2 st + hi) feeds QB products
+  auto qk = [&](f32x16 (&s)[QB][NKB], const uint16_t* ks) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[qb][kb] = f32x16{};
 #pragma unroll
     for (int st = 0; st < NQS; ++st)
 #pragma unroll
@@ -190,89 +250,117 @@ __global__ __launch_bounds__(kThreads, Bf16Cfg<D>::MINB) void fwd_bf16_kernel(Fw
         const int row = kb * 32 + l32;
         const bf16x8 a =
             *reinterpret_cast<const bf16x8*>(&ks[row * D + (((2 * st + hi) ^ k_swizzle<D>(row)) * 8)]);
-        s[kb] = mfma_bf16_32x32x16(a, qreg[st], s[kb]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma_bf16_32x32x16(a, qreg[qb][st], s[qb][kb]);
       }
   };
 
-  auto read_vt = [&](const uint16_t* vs, int kbase, int db) -> i16x4 {
+  // V^T A-operand via the transposed read: within each 16-lane group, source
+  // lane s addresses row kbase + s/4, columns dbase + 4 (s%4) .. +3; lane i of
+  // the group then receives column dbase + i, rows kbase .. kbase + 3.
+  const int grp = lane >> 4, sl = lane & 15;
+  const int v_row_in = sl >> 2;                        // + kbase
+  const int v_col_in = 16 * (grp & 1) + 4 * (sl & 3);  // + 32 db
+  auto read_vt = [&](const uint16_t* vs, int kbase, int db) __attribute__((always_inline)) -> i16x4 {
     const int row = kbase + v_row_in;
     const int col = 32 * db + v_col_in;
     const int e = row * D + (((col >> 3) ^ v_swizzle<D>(row)) << 3) + (col & 7);
     return lds_read_tr16(&vs[e]);
   };
 
-  float m_run = -INFINITY;  // exponent reference of row qrow (raw score units)
-  float l_run = 0.f;        // this half-wave's share of the running sum
-  f32x16 o[NDB];
+  // row max of one S^T block set: in-lane, then with the other half wave
+  auto rowmax = [&](const f32x16 (&s)[NKB]) -> float {
+    float mx = -INFINITY;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
-  const float c = p.c;
-  const float lazy = kLazyLog2 / c;  // the same threshold in raw score units
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmax3(mx, s[kb][r], s[kb][r + 1]);
+    return __builtin_fmaxf(mx, swap_halves(mx));
+  };
 
-  // one step for tile j: softmax of S_j (s_in), S_{j+1} into s_out,
-  // O += V_j^T P_j^T; the ring slots are passed as compile-time LDS objects:
+  float m_run[QB], l_run[QB];  // exponent reference (raw score units), this half-wave's row sum
+  f32x16 o[QB][NDB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[qb][db] = f32x16{};
+  }
+  const float c = p.c;
+  const float lazy = kLazyLog2 / c;  // the rescale threshold in raw score units
+
+  // one step for tile j: softmax of S_j (s_in, whose unmasked row max is in
+  // mx), S_{j+1} into s_out (its row max left in mx), O += V_j^T P_j^T.  The
+  // ring slots are passed as compile-time LDS objects:
   //   k_this: holds K_j until this step, then receives K_{j+2};  k_next: K_{j+1}
   //   v_this: V_j;  v_next: receives V_{j+1}
-  auto step = [&](int j, f32x16 (&s_in)[NKB], f32x16 (&s_out)[NKB], uint16_t* k_this, const uint16_t* k_next,
-                  const uint16_t* v_this, uint16_t* v_next) {
+  auto step = [&](int j, f32x16 (&s_in)[QB][NKB], f32x16 (&s_out)[QB][NKB], float (&mx)[QB], uint16_t* k_this,
+                  const uint16_t* k_next, const uint16_t* v_this, uint16_t* v_next) {
     wait_vmem_all();
     __syncthreads();  // V_j and K_{j+1} are in LDS; every wave is done with K_j and V_{j-1}
     if (j + 2 < ntiles) issue(rk, k_this, koff, j + 2);
     if (j + 1 < ntiles) issue(rv, v_next, voff, j + 1);
     const int key0 = j * BC;
-    const bool active = !CAUSAL || key0 <= q0 + kQW - 1;
-    if (!active) return;  // causal: every row of this wave lies above tile j (and all later ones)
+    if (CAUSAL && key0 > q0 + QW - 1) return;  // every row of this wave lies above tile j (and all later ones)
 
     // ---- mask (only tiles crossing the diagonal or the end of N) ----------
     const bool need_mask = (CAUSAL && key0 + BC - 1 > q0) || (key0 + BC > N);
     if (need_mask) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool dead = (CAUSAL && key > qrow) || key >= N;
-          s_in[kb][r] = dead ? -INFINITY : s_in[kb][r];
-        }
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const bool dead = (CAUSAL && key > qrow[qb]) || key >= N;
+            s_in[qb][kb][r] = dead ? -INFINITY : s_in[qb][kb][r];
+          }
+        mx[qb] = rowmax(s_in[qb]);
+      }
     }
-    // ---- row max and the lazy rescale decision --------------------------------
-    float mx = -INFINITY;
+    // ---- lazy rescale ---------------------------------------------------------
+    bool grow = false;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int qb = 0; qb < QB; ++qb) grow |= mx[qb] > m_run[qb] + lazy;
+    if (__any(grow)) {
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmax3(mx, s_in[kb][r], s_in[kb][r + 1]);
-    mx = __builtin_fmaxf(mx, swap_halves(mx));
-    if (__any(mx > m_run + lazy)) {
-      const float m_new = __builtin_fmaxf(m_run, mx);
-      const float alpha = exp2_fast((m_run - m_new) * c);  // 0 on the first tile
-      l_run *= alpha;
+      for (int qb = 0; qb < QB; ++qb) {
+        const float m_new = __builtin_fmaxf(m_run[qb], mx[qb]);
+        const float alpha = exp2_fast((m_run[qb] - m_new) * c);  // 0 on the first tile
+        l_run[qb] *= alpha;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-      m_run = m_new;
+        for (int db = 0; db < NDB; ++db) o[qb][db] *= alpha;
+        m_run[qb] = m_new;
+      }
     }
-    const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
 
     // ---- one branch-free block: S_{j+1} = K_{j+1} Q^T on the matrix cores
-    // while exp2 / bf16 cast / row sum of S_j run on the vector ALUs.  For the
-    // last tile the product reads a stale slot and is never used.
+    // while exp2 / bf16 cast / row sums of S_j run on the vector ALUs; then
+    // O^T += V_j^T P_j^T while the row max of S_{j+1} is taken.  For the
+    // last tile the first product reads a stale slot and is never used.
     qk(s_out, k_next);
-    bf16x8 pb[NPS];
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};  // fp32 partial row sums (four short chains)
+    bf16x8 pb[QB][NPS];
 #pragma unroll
-    for (int ks = 0; ks < NPS; ++ks) {
-      const int kb = ks >> 1, r0 = (ks & 1) * 8;
-      u32x4 t;
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mc = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb] * c;
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};  // fp32 partial row sums (four short chains)
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const float e0 = exp2_fast(__builtin_fmaf(s_in[kb][r0 + 2 * h], c, -mc));
-        const float e1 = exp2_fast(__builtin_fmaf(s_in[kb][r0 + 2 * h + 1], c, -mc));
-        t[h] = pack_bf16x2(e0, e1);
-        ls[h] += e0 + e1;
+      for (int ks = 0; ks < NPS; ++ks) {
+        const int kb = ks >> 1, r0 = (ks & 1) * 8;
+        u32x4 t;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const float e0 = exp2_fast(__builtin_fmaf(s_in[qb][kb][r0 + 2 * h], c, -mc));
+          const float e1 = exp2_fast(__builtin_fmaf(s_in[qb][kb][r0 + 2 * h + 1], c, -mc));
+          t[h] = pack_bf16x2(e0, e1);
+          ls[h] += e0 + e1;
+        }
+        pb[qb][ks] = __builtin_bit_cast(bf16x8, t);
       }
-      pb[ks] = __builtin_bit_cast(bf16x8, t);
+      l_run[qb] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-    // ---- O^T += V_j^T P_j^T ---------------------------------------------------
     // k-step ks covers keys 16ks + 4hi + 0..3 (first read) and 16ks + 8 + 4hi
     // + 0..3 (second read): the key order of the P^T registers.
 #pragma unroll
@@ -282,46 +370,57 @@ __global__ __launch_bounds__(kThreads, Bf16Cfg<D>::MINB) void fwd_bf16_kernel(Fw
         const i16x4 a0 = read_vt(v_this, 16 * ks + 4 * hi, db);
         const i16x4 a1 = read_vt(v_this, 16 * ks + 8 + 4 * hi, db);
         const u32x2 w0 = __builtin_bit_cast(u32x2, a0), w1 = __builtin_bit_cast(u32x2, a1);
-        const u32x4 a = {w0[0], w0[1], w1[0], w1[1]};
-        o[db] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, a), pb[ks], o[db]);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma_bf16_32x32x16(a, pb[qb][ks], o[qb][db]);
       }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mx[qb] = rowmax(s_out[qb]);
+    schedule_step<NKB * NQS, NPS * NDB, QB>();
   };
 
-  // ---- prologue: K_0, V_0, K_1 in flight; S_0 -----------------------------
-  f32x16 sa[NKB], sb[NKB];
+  // ---- prologue: K_0, V_0, K_1 in flight; S_0 and its row max ---------------
+  f32x16 sa[QB][NKB], sb[QB][NKB];
+  float mx[QB];
   issue(rk, Ks0, koff, 0);
   issue(rv, Vs0, voff, 0);
   if (ntiles > 1) issue(rk, Ks1, koff, 1);
   wait_vmem_all();
   __syncthreads();
   qk(sa, Ks0);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) mx[qb] = rowmax(sa[qb]);
   for (int j = 0; j < ntiles; j += 2) {
-    step(j, sa, sb, Ks0, Ks1, Vs0, Vs1);
-    if (j + 1 < ntiles) step(j + 1, sb, sa, Ks1, Ks0, Vs1, Vs0);
+    step(j, sa, sb, mx, Ks0, Ks1, Vs0, Vs1);
+    if (j + 1 < ntiles) step(j + 1, sb, sa, mx, Ks1, Ks0, Vs1, Vs0);
   }
 
   // ---- epilogue: O / l, lse = m * scale + ln l ----------------------------
-  const float l_tot = l_run + swap_halves(l_run);
-  if (qrow < N) {
-    const float inv = 1.f / l_tot;
-    float* orow = p.o + base + (size_t)qrow * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = l_run[qb] + swap_halves(l_run[qb]);
+    if (qrow[qb] < N) {
+      const float inv = 1.f / l_tot;
+      float* orow = p.o + base + (size_t)qrow[qb] * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 val = {o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
-                           o[db][4 * g + 3] * inv};
-        *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * g + 4 * hi) = val;
-      }
-    if (hi == 0) p.lse[(size_t)bh * N + qrow] = m_run * p.scale + __logf(l_tot);
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 val = {o[qb][db][4 * g] * inv, o[qb][db][4 * g + 1] * inv, o[qb][db][4 * g + 2] * inv,
+                             o[qb][db][4 * g + 3] * inv};
+          *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * g + 4 * hi) = val;
+        }
+      if (hi == 0) p.lse[(size_t)bh * N + qrow[qb]] = m_run[qb] * p.scale + __logf(l_tot);
+    }
   }
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdBf16Params& p, hipStream_t stream) {
-  const int nq = (p.N + kBR - 1) / kBR;
+  constexpr int BR = rows_per_workgroup<D>();
+  const int nq = (p.N + BR - 1) / BR;
   const unsigned grid = (unsigned)nq * (unsigned)p.B * (unsigned)p.H;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(grid), dim3(Bf16Cfg<D>::NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 

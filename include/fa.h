@@ -88,7 +88,12 @@ int fa_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* ls
  *   x8      : uint8 E4M3 (OCP e4m3fn) codes of y / s:
  *             [B, H, N, d] by default, or with FA_PREP_TRANSPOSE the
  *             transposed [B, H, d, ld] with ld = fa_fp8_vt_ld(N); columns
- *             N..ld-1 are written as zero codes.
+ *             N..ld-1 are written as zero codes.  In the transposed layout
+ *             the keys of each row are stored in groups of four (one 32-bit
+ *             word each) and, within every aligned run of 64 keys, word w
+ *             holds key group 2 (w % 8) + w / 8: the even groups first, then
+ *             the odd ones, which is the key order of fa_fwd_fp8's PV
+ *             operand.
  *   x_scale : fp32 [B, H, ceil(N / 128)]: s = amax(|y|) / 448 over each block
  *             of 128 rows (all of d); s = 1 for an all-zero block.  With
  *             FA_PREP_POW2_SCALE, s = 2^ceil(log2(amax / 448)) instead (the

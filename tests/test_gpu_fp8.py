@@ -41,10 +41,23 @@ def _codes_close(got, ref, label, max_frac=1e-3):
         assert np.all(np.abs((gi & 0x7F) - (ri & 0x7F)) <= 1), label
 
 
+def unpermute_vt(vt):
+    """Undo the key-group order of the transposed V layout: within every 64
+    keys, output word w holds key group 2 (w % 8) + w // 8."""
+    vt = np.asarray(vt)
+    *lead, ld = vt.shape
+    words = vt.reshape(*lead, ld // 64, 16, 4)
+    w = np.arange(16)
+    groups = 2 * (w % 8) + w // 8
+    out = np.empty_like(words)
+    out[..., groups, :] = words
+    return out.reshape(*lead, ld)
+
+
 def _dequant_gpu(x8, sc, N, transpose=False):
     codes = x8.cpu().numpy()
     if transpose:
-        codes = np.ascontiguousarray(np.swapaxes(codes[..., :N], 2, 3))
+        codes = np.ascontiguousarray(np.swapaxes(unpermute_vt(codes)[..., :N], 2, 3))
     s = sc.cpu().numpy().astype(np.float64)
     srow = np.repeat(s, 128, axis=2)[:, :, :N, None]
     return codes, e4m3_decode(codes) * srow
@@ -68,7 +81,7 @@ def test_prep_codes_and_scales(gpu_lib, N, mode):
     vc_ref, vs_ref, _ = quantize_fp8(v, per_tensor=per_tensor, pow2=True)
     torch.cuda.synchronize()
     assert tuple(v8t.shape) == (B, H, d, fa.fp8_vt_ld(N))
-    vt = v8t.cpu().numpy()
+    vt = unpermute_vt(v8t.cpu().numpy())
     assert np.all(vt[..., N:] == 0)
     # power-of-two scales and codes are exact: bit-equal
     np.testing.assert_array_equal(vs.cpu().numpy(), vs_ref.astype(np.float32))
