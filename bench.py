@@ -15,7 +15,14 @@ non-causal and once causal, inputs resident in HBM.  FLOPs are counted as
 * ``cpu_baseline``: the CPU fp64 oracle timed on a bounded sample of the
   same step on this host.
 
+``roofline.traffic`` is the kernel's HBM bytes per launch read by two
+rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE, each scaled by what the
+counter reads for a 256 MiB device copy), recorded in
+profiles/fwd_bf16_std_noncausal_traffic.md together with the SHA-256 of the
+kernel's sources; it is null when those sources changed since.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
+                       [--copy-calibration]
 """
 
 from __future__ import annotations
@@ -31,6 +38,12 @@ PEAK_FP8 = 5033.2
 PEAK_HBM = 8000.0  # GB/s
 METRIC = "attention fwd TFLOPS (bf16, fp8) at d=128 vs N, and % of MFMA peak"
 GPU_HOLD_CYCLES = 20_000_000  # a short device-side spin before each timed region
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# HBM traffic of the dominant kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# passes; valid only while the kernel sources hash to what was profiled
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_bf16_std_noncausal_traffic.md")
+TRAFFIC_SOURCES = ("exact_attention_73_amd/csrc/fa_fwd_bf16.hip", "exact_attention_73_amd/csrc/fa_device.h")
+COPY_CALIBRATION_BYTES = 256 << 20
 
 
 def fwd_flops(B, H, N, d, causal):
@@ -57,6 +70,33 @@ def _time_launches(fn, reps, warmup):
     return sum(ts) / len(ts), ts[len(ts) // 2]
 
 
+def kernel_sources_sha256():
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic():
+    """Bytes per launch (FETCH + WRITE, calibrated) from the committed counter
+    summary, or None when it is missing or the kernel changed since."""
+    try:
+        fields = {}
+        with open(TRAFFIC_SUMMARY) as f:
+            for ln in f:
+                if ln.startswith("- `") and "`: " in ln:
+                    key, val = ln[3:].split("`: ", 1)
+                    fields[key] = val.strip().strip("`")
+        if fields.get("kernel_sources_sha256") != kernel_sources_sha256():
+            return None
+        return int(fields["fetch_bytes_per_launch"]) + int(fields["write_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -64,6 +104,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="skip the sweep and FP8 legs (for profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region, copy 256 MiB device-to-device once, untimed, so that a "
+                         "counter pass sees a kernel of known traffic beside the attention kernels")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (every (batch, head) pair is "
@@ -160,6 +203,14 @@ def main():
         }
         del q, k, v, q8, k8, v8t
 
+    if args.copy_calibration:
+        src = torch.ones(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(B, H, N, d, w.seed)
@@ -192,7 +243,8 @@ def main():
             "peak": PEAK_BF16,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16, 4),
-            "traffic": None,
+            "traffic": profiled_traffic(),
+            "traffic_unit": "bytes per launch",
         },
         "legs": legs,
         "cpu_baseline": cpu,
