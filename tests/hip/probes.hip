@@ -21,6 +21,12 @@ __global__ void k_mfma_fp8(const i32x8* a, const i32x8* b, f32x16* c, int sa, in
   c[l] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[l], b[l], f32x16{}, 0, 0, 0, sa, 0, sb);
 }
 
+// the same with one E8M0 scale per lane for each operand (sa[l], sb[l])
+__global__ void k_mfma_fp8_lanescale(const i32x8* a, const i32x8* b, f32x16* c, const int* sa, const int* sb) {
+  const int l = threadIdx.x;
+  c[l] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[l], b[l], f32x16{}, 0, 0, 0, sa[l], 0, sb[l]);
+}
+
 __global__ void k_mfma_fp8_unscaled(const i32x8* a, const i32x8* b, f32x16* c) {
   const int l = threadIdx.x;
   c[l] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[l], b[l], f32x16{}, 0, 0, 0, 0, 0, 0);
@@ -78,6 +84,11 @@ int probe_mfma_bf16(const void* a, const void* b, float* c, void* s) {
 }
 int probe_mfma_fp8(const void* a, const void* b, float* c, int sa, int sb, void* s) {
   hipLaunchKernelGGL(k_mfma_fp8, dim3(1), dim3(64), 0, (hipStream_t)s, (const i32x8*)a, (const i32x8*)b, (f32x16*)c, sa, sb);
+  return hipGetLastError();
+}
+int probe_mfma_fp8_lanescale(const void* a, const void* b, float* c, const int* sa, const int* sb, void* s) {
+  hipLaunchKernelGGL(k_mfma_fp8_lanescale, dim3(1), dim3(64), 0, (hipStream_t)s, (const i32x8*)a, (const i32x8*)b,
+                     (f32x16*)c, sa, sb);
   return hipGetLastError();
 }
 int probe_mfma_fp8_unscaled(const void* a, const void* b, float* c, void* s) {

@@ -20,8 +20,8 @@ def probes():
     if not torch.cuda.is_available():
         pytest.fail("GPU test collected on a machine without a GPU")
     lib = ctypes.CDLL(LIB)
-    for n in ("probe_mfma_bf16", "probe_mfma_fp8", "probe_mfma_fp8_unscaled", "probe_cvt_fp8", "probe_swap_halves",
-              "probe_tr16", "probe_load_lds"):
+    for n in ("probe_mfma_bf16", "probe_mfma_fp8", "probe_mfma_fp8_lanescale", "probe_mfma_fp8_unscaled",
+              "probe_cvt_fp8", "probe_swap_halves", "probe_tr16", "probe_load_lds"):
         getattr(lib, n).restype = ctypes.c_int
     return lib
 
@@ -78,6 +78,54 @@ def test_mfma_fp8_32x32x64_layout_and_scales(probes, sa, sb):
         for r in range(16):
             got[8 * (r // 4) + 4 * (l // 32) + (r % 4), l % 32] = c[l, r]
     np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-3 * np.abs(ref).max())
+
+
+def test_mfma_fp8_per_lane_scales(probes):
+    """Per-lane E8M0 scales: with lane L holding bytes j = 0..31 of row/column
+    L % 32 (k = 32 (L // 32) + j, the layout the products above verify), byte
+    j takes the scale of lane (L % 32) + 32 (j // 16) -- bytes 0..15 the
+    first half-wave's, bytes 16..31 the second's.  So equal scales in lanes
+    n and n + 32 scale column n (or row n) of the product exactly, which is
+    what the FP8 forward relies on for its per-query-row power of two."""
+    rng = np.random.default_rng(11)
+    A = rng.integers(0, 256, size=(32, 64)).astype(np.uint8)
+    B = rng.integers(0, 256, size=(64, 32)).astype(np.uint8)
+    A[(A & 0x7F) == 0x7F] = 0x38
+    B[(B & 0x7F) == 0x7F] = 0x38
+    sa = rng.integers(120, 135, size=64).astype(np.int32)
+    sb = rng.integers(110, 140, size=64).astype(np.int32)
+    a = np.zeros((64, 32), np.uint8)
+    b = np.zeros((64, 32), np.uint8)
+    for l in range(64):
+        a[l] = A[l % 32, 32 * (l // 32): 32 * (l // 32) + 32]
+        b[l] = B[32 * (l // 32): 32 * (l // 32) + 32, l % 32]
+    c = torch.zeros(64, 16, dtype=torch.float32, device="cuda")
+    assert probes.probe_mfma_fp8_lanescale(_p(torch.from_numpy(a).cuda()), _p(torch.from_numpy(b).cuda()), _p(c),
+                                           _p(torch.from_numpy(sa).cuda()), _p(torch.from_numpy(sb).cuda()), _s()) == 0
+    torch.cuda.synchronize()
+    cc = c.cpu().numpy()
+    got = np.zeros((32, 32))
+    for l in range(64):
+        for r in range(16):
+            got[8 * (r // 4) + 4 * (l // 32) + (r % 4), l % 32] = cc[l, r]
+    sel = (np.arange(64) % 32) // 16  # which half-wave's scale byte k takes
+    Ad = e4m3_decode(A) * 2.0 ** (sa[np.arange(32)[:, None] + 32 * sel[None, :]] - 127)
+    Bd = e4m3_decode(B) * 2.0 ** (sb[np.arange(32)[None, :] + 32 * sel[:, None]] - 127)
+    ref = Ad @ Bd
+    np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-4 * np.abs(ref).max())
+    # the property the forward kernel uses: equal scales in both halves
+    sb2 = np.concatenate([sb[:32], sb[:32]]).astype(np.int32)
+    c2 = torch.zeros(64, 16, dtype=torch.float32, device="cuda")
+    assert probes.probe_mfma_fp8_lanescale(_p(torch.from_numpy(a).cuda()), _p(torch.from_numpy(b).cuda()), _p(c2),
+                                           _p(torch.from_numpy(np.full(64, 127, np.int32)).cuda()),
+                                           _p(torch.from_numpy(sb2).cuda()), _s()) == 0
+    torch.cuda.synchronize()
+    cc = c2.cpu().numpy()
+    for l in range(64):
+        for r in range(16):
+            got[8 * (r // 4) + 4 * (l // 32) + (r % 4), l % 32] = cc[l, r]
+    ref2 = (e4m3_decode(A) @ e4m3_decode(B)) * 2.0 ** (sb[None, :32] - 127)
+    np.testing.assert_allclose(got, ref2, rtol=1e-5, atol=1e-4 * np.abs(ref2).max())
 
 
 def test_mfma_fp8_unscaled_form(probes):
