@@ -39,8 +39,15 @@ What the pages fix, and the readings taken where they are silent:
   P_q = E4M3(P * 2^7 * mu) / (2^7 * mu), so that P * 2^7 * mu < 256 < 448
   never saturates, small probabilities stay out of the subnormal range, and
   the remaining factor 2^e * 2^-7 is an exact power of two.  The row sum l
-  is taken from the unquantised P.  The reading is pinned only in the sense
-  that with quantisation switched off the emulation equals
+  is taken from the unquantised P.  The exponent reference of P is the
+  running row max rounded up to a whole power of two, M = ln 2 *
+  ceil(m / ln 2) (the online-softmax recurrence is exact for any reference
+  that bounds the scores seen so far): P = exp(S - M) lies in (0, 1], the
+  factors between tiles are exact powers of two, and since E4M3 rounding
+  commutes with powers of two in its normal range, P_q * e^M does not depend
+  on which whole power is taken except for values in the subnormal range.
+  The reading is pinned by a hand-worked two-key case and in the sense that
+  with quantisation switched off the emulation equals
   :func:`oracle.attention.attention_ref`.
 """
 
@@ -68,6 +75,7 @@ __all__ = [
 E4M3_MAX = 448.0  # P2 section 三.3
 SCALE_BLOCK = 128  # rows per scale block
 P_PRESCALE_EXP = 7  # P is scaled by 2^7 * mantissa(s_V) before rounding (parity unpinned)
+LN2 = float(np.log(2.0))
 
 
 def e4m3_decode(codes) -> np.ndarray:
@@ -224,7 +232,9 @@ def fp8_attention_emulate(qh, kh, vh, causal: bool = False, scale=None, Bc: int 
     quantised against; ``Bc`` must divide the scale block).  With
     ``quantize_p`` the PV product uses P_q = E4M3(P * f) / f with
     f = 2^7 * mantissa(s_V) of the key's V scale block (``v_scale``
-    ``[B, H, ceil(N / block)]``), while ``l`` sums the unquantised P.
+    ``[B, H, ceil(N / block)]``), while ``l`` sums the unquantised P.  P is
+    taken against the running max rounded up to a whole power of two,
+    M = ln 2 * ceil(m / ln 2), so P is in (0, 1].
     """
     qh, kh, vh = to_f64(qh), to_f64(kh), to_f64(vh)
     B, H, N, d = qh.shape
@@ -239,7 +249,8 @@ def fp8_attention_emulate(qh, kh, vh, causal: bool = False, scale=None, Bc: int 
     lse = np.empty((B, H, N))
     for b in range(B):
         for h in range(H):
-            m = np.full(N, -np.inf)
+            m = np.full(N, -np.inf)  # running max
+            r = np.full(N, -np.inf)  # exponent reference: m rounded up to a whole power of two
             l = np.zeros(N)
             acc = np.zeros((N, vh.shape[3]))
             for j0 in range(0, Nk, Bc):
@@ -249,8 +260,9 @@ def fp8_attention_emulate(qh, kh, vh, causal: bool = False, scale=None, Bc: int 
                     S = np.where(np.arange(j0, j1)[None, :] > qi[:, None], -np.inf, S)
                 m_new = np.maximum(m, S.max(axis=1))
                 dead = np.isneginf(m_new)
-                safe = np.where(dead, 0.0, m_new)
-                alpha = np.where(dead, 1.0, np.exp(m - safe))
+                r_new = np.where(dead, -np.inf, np.ceil(m_new / LN2) * LN2)
+                safe = np.where(dead, 0.0, r_new)
+                alpha = np.where(dead, 1.0, np.exp(r - safe))
                 P = np.where(dead[:, None], 0.0, np.exp(S - safe[:, None]))
                 l = alpha * l + P.sum(axis=1)
                 if quantize_p:
@@ -259,9 +271,9 @@ def fp8_attention_emulate(qh, kh, vh, causal: bool = False, scale=None, Bc: int 
                 else:
                     Pq = P
                 acc = alpha[:, None] * acc + Pq @ vh[b, h, j0:j1]
-                m = m_new
+                m, r = m_new, r_new
             o[b, h] = acc / l[:, None]
-            lse[b, h] = m + np.log(l)
+            lse[b, h] = r + np.log(l)
     return o, lse
 
 

@@ -205,6 +205,40 @@ def test_fp8_error_is_small_and_ordered_on_outliers():
     assert rms["block+had"] <= rms["tensor"]
 
 
+def test_p_quantisation_worked_example():
+    """One query, two keys, d = 1, scale 1: scores ln 3 and ln 3 + ln 0.3.
+    By hand: the running max ln 3 is log2(3) = 1.58 in base-2 units, so the
+    reference is 2^2 and P = (3/4, 0.225); times 2^7: 96 (exact) and 28.8,
+    which rounds to 28 on the E4M3 grid (step 2 in [16, 32)).  So P_q =
+    (0.75, 0.21875), l = 0.975 from the unrounded P, O = P_q V / l and
+    lse = ln(3.9).  (Taking the reference at the exact max instead would give
+    P = (1, 0.3) -> 128, 38.4 -> 40 and O = (1, 0.3125) / 1.3.)"""
+    qh = np.ones((1, 1, 1, 1))
+    kh = np.array([np.log(3.0), np.log(3.0) + np.log(0.3)]).reshape(1, 1, 2, 1)
+    vh = np.eye(2).reshape(1, 1, 2, 2)
+    o, lse = fp8_attention_emulate(qh, kh, vh, scale=1.0, Bc=2, v_scale=np.ones((1, 1, 1)), block=128)
+    np.testing.assert_allclose(o[0, 0, 0], [0.75 / 0.975, 0.21875 / 0.975], rtol=1e-12)
+    np.testing.assert_allclose(lse[0, 0, 0], np.log(3.9), rtol=1e-12)
+
+
+def test_p_quantisation_invariant_to_the_power_of_two_reference():
+    """E4M3 rounding commutes with powers of two in the normal range: shifting
+    every score by a whole number of ln 2 moves the reference by the same
+    amount and leaves O unchanged (scores here stay far from the subnormal
+    range of P)."""
+    g = np.random.default_rng(3)
+    B, H, N, d = 1, 1, 96, 16
+    qh, kh, vh = (g.standard_normal((B, H, N, d)) * 0.3 for _ in range(3))
+    vs = np.ones((1, 1, 1))
+    o1, l1 = fp8_attention_emulate(qh, kh, vh, scale=1.0, Bc=32, v_scale=vs)
+    # add 5 ln 2 to every score via an extra feature: q gets a 1, k gets 5 ln 2
+    q2 = np.concatenate([qh, np.ones((B, H, N, 1))], axis=3)
+    k2 = np.concatenate([kh, np.full((B, H, N, 1), 5 * np.log(2.0))], axis=3)
+    o2, l2 = fp8_attention_emulate(q2, k2, vh, scale=1.0, Bc=32, v_scale=vs)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(l2, l1 + 5 * np.log(2.0), rtol=1e-12)
+
+
 def test_scale_mantissa_closed_form():
     from oracle import scale_mantissa
 
