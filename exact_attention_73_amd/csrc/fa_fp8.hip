@@ -337,7 +337,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
   };
 
   float ks_next = 0.f, vs_next = 0.f;  // K and V scales of the next tile to process
-  float m_run = -INFINITY;  // running max of the log2-domain scores of row qrow
+  // P's exponent reference: the running max of the log2-domain scores of row
+  // qrow rounded up to a whole number (P = 2^(t - m_ref) in (0, 1]).  O and l
+  // are accumulated against m_base, the reference of the first tile; each
+  // tile's P^T enters the PV product scaled by 2^(m_ref - m_base), exactly,
+  // through the instruction's per-lane E8M0 scale of the B operand (both
+  // half-waves of a query row carry the same value), so O is never rescaled.
+  float m_ref = -INFINITY;
+  float m_base = 0.f;
   float l_run = 0.f;
   f32x16 o[NDB];
 #pragma unroll
@@ -366,7 +373,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
     const int v_exp = (int)((svb >> 23) & 0xffu);                          // E8M0 exponent of s_V
     const float mu = __uint_as_float((svb & 0x007fffffu) | 0x3f800000u);  // s_V mantissa in [1, 2)
     const float pbias = 7.f + __builtin_amdgcn_logf(mu);                  // log2(2^7 mu); 7 for power-of-two s_V
-    const float inv_f = 1.f / (128.f * mu);
+    const float inv_f = __builtin_amdgcn_rcpf(128.f * mu);  // exact for the power-of-two V scales
 
     const bool need_mask = (CAUSAL && key0 + kBC - 1 > q0) || (key0 + kBC > N);
     if (need_mask) {
@@ -385,17 +392,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
 #pragma unroll
       for (int r = 0; r < 16; r += 2) mx = fmax3(mx, s_in[kb][r], s_in[kb][r + 1]);
     mx = __builtin_fmaxf(mx, swap_halves(mx)) * ct;  // ct > 0; -inf stays -inf
-    // the exact running max (probabilities stay in (0, 1]); skip the rescale
-    // when no row of the wave grew, where every alpha would be exactly 1
-    if (__any(mx > m_run)) {
-      const float m_new = __builtin_fmaxf(m_run, mx);
-      const float alpha = exp2_fast(m_run - m_new);  // 0 on the first tile
-      l_run *= alpha;
+    m_ref = __builtin_fmaxf(m_ref, __builtin_ceilf(mx));
+    // every row sees key 0 in tile 0, so its reference is finite from there on
+    if (j == 0) m_base = (m_ref == -INFINITY) ? 0.f : m_ref;
+    float shift = (m_ref == -INFINITY) ? 0.f : m_ref - m_base;  // a whole number >= 0
+    if (__any(shift > 64.f)) {
+      // rare (scores grew by more than 2^64 over the first tile's): move the
+      // base so O and l stay far from the fp32 range; an exact power of two
+      const float f = exp2_fast(-shift);
+      l_run *= f;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-      m_run = m_new;
+      for (int db = 0; db < NDB; ++db) o[db] *= f;
+      m_base += shift;
+      shift = 0.f;
     }
-    const float moff = ((m_run == -INFINITY) ? 0.f : m_run) - pbias;
+    const int ishift = (int)shift;
+    const float moff = ((m_ref == -INFINITY) ? 0.f : m_ref) - pbias;
 
     qk(s_out, k_next);  // S_{j+1}: matrix cores, while the exps below run
     i32x8 pb;
@@ -410,7 +422,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
       ls[w & 3] += (e0 + e1) + (e2 + e3);
       pb[w] = (int)cvt_e4m3x4(e0, e1, e2, e3);
     }
-    l_run += ((ls[0] + ls[1]) + (ls[2] + ls[3])) * inv_f;
+    l_run += ((ls[0] + ls[1]) + (ls[2] + ls[3])) * __builtin_amdgcn_ldexpf(inv_f, ishift);
     // O^T += V^T P^T: lane half hi reads the 32 bytes [32 hi, 32 hi + 32) of
     // row d, which hold keys 8w + 4hi .. +3 for w = 0..7 (the prep's order)
 #pragma unroll
@@ -422,7 +434,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
       const u32x4 c1 = *reinterpret_cast<const u32x4*>(vrow + (((2 * hi + 1) ^ sw) * 16));
       const i32x8 a = {(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3],
                        (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
-      o[db] = mfma_fp8_32x32x64(a, pb, o[db], v_exp, 127 - 7);
+      o[db] = mfma_fp8_32x32x64(a, pb, o[db], v_exp, 127 - 7 + ishift);
     }
   };
 
@@ -452,7 +464,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
                            o[db][4 * g + 3] * inv};
         *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * g + 4 * hi) = val;
       }
-    if (hi == 0) p.lse[(size_t)bh * N + qrow] = m_run * 0.6931471805599453f + __logf(l_tot);
+    if (hi == 0) p.lse[(size_t)bh * N + qrow] = m_base * 0.6931471805599453f + __logf(l_tot);
   }
 }
 
