@@ -238,6 +238,38 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 __device__ __forceinline__ int k8_swizzle(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int v8_swizzle(int d) { return (d >> 2) & 3; }
 
+// Instruction-group order of one forward step (compiler scheduling hints;
+// masks: 0x008 matrix, 0x100 LDS read, 0x002 vector ALU).  First block: the
+// K operand reads, then the four S_{j+1} products each followed by a share
+// of the softmax of S_j.  Second block: the V^T reads and the four PV
+// products with the row max of S_{j+1} between them.
+#ifndef FA8_SCHED
+#define FA8_SCHED 0
+#endif
+#ifndef FA8_VPM
+#define FA8_VPM 30
+#endif
+__device__ __forceinline__ void schedule_fp8_qk() {
+  if constexpr (FA8_SCHED) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, FA8_VPM, 0);
+    }
+  }
+}
+__device__ __forceinline__ void schedule_fp8_pv() {
+  if constexpr (FA8_SCHED) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+  }
+}
+
 template <bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
   constexpr int D = 128;
@@ -352,8 +384,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
 
   // one step for tile j: softmax of S_j (s_in), S_{j+1} into s_out,
   // O += V_j^T P_j^T; ring slots as in the bf16 kernel.
-  auto step = [&](int j, f32x16 (&s_in)[NKB], f32x16 (&s_out)[NKB], uint8_t* k_this, const uint8_t* k_next,
-                  const uint8_t* v_this, uint8_t* v_next) __attribute__((always_inline)) {
+  // raw row max (before the scale) of one S^T tile: in-lane, then with the other half wave
+  auto rowmax = [&](const f32x16 (&sv)[NKB]) __attribute__((always_inline)) -> float {
+    float m = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) m = fmax3(m, sv[kb][r], sv[kb][r + 1]);
+    return __builtin_fmaxf(m, swap_halves(m));
+  };
+
+  // mx: raw row max of s_in on entry, of s_out on exit (taken at the end of
+  // the step so that the S_{j+1} products stay in this step's block)
+  auto step = [&](int j, f32x16 (&s_in)[NKB], f32x16 (&s_out)[NKB], float& mx, uint8_t* k_this,
+                  const uint8_t* k_next, const uint8_t* v_this, uint8_t* v_next) __attribute__((always_inline)) {
     const int key0 = j * kBC;
     wait_vmem_all();
     __syncthreads();
@@ -385,28 +429,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
           const bool dead = (CAUSAL && key > qrow) || key >= N;
           s_in[kb][r] = dead ? -INFINITY : s_in[kb][r];
         }
+      mx = rowmax(s_in);
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmax3(mx, s_in[kb][r], s_in[kb][r + 1]);
-    mx = __builtin_fmaxf(mx, swap_halves(mx)) * ct;  // ct > 0; -inf stays -inf
-    m_ref = __builtin_fmaxf(m_ref, __builtin_ceilf(mx));
+    m_ref = __builtin_fmaxf(m_ref, __builtin_ceilf(mx * ct));  // ct > 0; -inf stays -inf
     // every row sees key 0 in tile 0, so its reference is finite from there on
     if (j == 0) m_base = (m_ref == -INFINITY) ? 0.f : m_ref;
     float shift = (m_ref == -INFINITY) ? 0.f : m_ref - m_base;  // a whole number >= 0
-    if (__any(shift > 64.f)) {
-      // rare (scores grew by more than 2^64 over the first tile's): move the
-      // base so O and l stay far from the fp32 range; an exact power of two
-      const float f = exp2_fast(-shift);
-      l_run *= f;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db] *= f;
-      m_base += shift;
-      shift = 0.f;
-    }
-    const int ishift = (int)shift;
     const float moff = ((m_ref == -INFINITY) ? 0.f : m_ref) - pbias;
 
     qk(s_out, k_next);  // S_{j+1}: matrix cores, while the exps below run
@@ -422,7 +450,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
       ls[w & 3] += (e0 + e1) + (e2 + e3);
       pb[w] = (int)cvt_e4m3x4(e0, e1, e2, e3);
     }
-    l_run += ((ls[0] + ls[1]) + (ls[2] + ls[3])) * __builtin_amdgcn_ldexpf(inv_f, ishift);
+    const float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    schedule_fp8_qk();
+    // The test also reads lsum and the last S_{j+1} product (finite scores:
+    // adding 0 * s is exact), which keeps the products and the softmax in
+    // this block, ahead of the branch, for the interleave above.
+    if (__any(shift + 0.f * (s_out[0][15] + s_out[NKB - 1][15]) > 64.f && lsum >= 0.f)) {
+      // rare (scores grew by more than 2^64 over the first tile's): move the
+      // base so O and l stay far from the fp32 range; an exact power of two
+      const float f = exp2_fast(-shift);
+      l_run *= f;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] *= f;
+      m_base += shift;
+      shift = 0.f;
+    }
+    const int ishift = (int)shift;
+    l_run += lsum * __builtin_amdgcn_ldexpf(inv_f, ishift);
     // O^T += V^T P^T: lane half hi reads the 32 bytes [32 hi, 32 hi + 32) of
     // row d, which hold keys 8w + 4hi .. +3 for w = 0..7 (the prep's order)
 #pragma unroll
@@ -436,9 +480,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
                        (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
       o[db] = mfma_fp8_32x32x64(a, pb, o[db], v_exp, 127 - 7 + ishift);
     }
+    mx = rowmax(s_out);
+    schedule_fp8_pv();
   };
 
   f32x16 sa[NKB], sb[NKB];
+  float mx;
   issue_k(Ks0, 0);
   issue_v(Vs0, 0);
   ks_next = ks[0];
@@ -447,9 +494,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
   wait_vmem_all();
   __syncthreads();
   qk(sa, Ks0);
+  mx = rowmax(sa);
   for (int j = 0; j < ntiles; j += 2) {
-    step(j, sa, sb, Ks0, Ks1, Vs0, Vs1);
-    if (j + 1 < ntiles) step(j + 1, sb, sa, Ks1, Ks0, Vs1, Vs0);
+    step(j, sa, sb, mx, Ks0, Ks1, Vs0, Vs1);
+    if (j + 1 < ntiles) step(j + 1, sb, sa, mx, Ks1, Ks0, Vs1, Vs0);
   }
 
   const float l_tot = l_run + swap_halves(l_run);
