@@ -20,13 +20,17 @@
 // Forward: same decomposition, data path and online softmax as the bf16
 // kernel (one workgroup of 4 waves per 128 query rows, direct-to-LDS K and
 // V^T rings with K one tile ahead, S^T = K Q^T and O^T = V^T P^T on
-// v_mfma_f32_32x32x64_f8f6f4 with fp32 accumulation and softmax state); the
-// running max is exact (the rescale is skipped only when no row grew), so
-// the probabilities stay in (0, 1].  Scores
-// are descaled by folding s_Q,i * s_K,j into the exp2 constant of each
-// tile; probabilities are produced directly as P * 2^7 * mu_j (exp2 bias)
-// and cast to E4M3, and the PV instruction's block exponents supply
-// 2^-7 (P) and 2^e_j (V), where s_V,j = mu_j * 2^e_j.
+// v_mfma_f32_32x32x64_f8f6f4 with fp32 accumulation and softmax state).
+// The exponent reference of P is the running max rounded up to a whole
+// number in the log2 domain, so P is in (0, 1] and every change of
+// reference is an exact power of two: O and l are accumulated against the
+// first tile's reference and each tile's P^T enters the PV product scaled
+// by 2^(reference - base) through the instruction's per-lane E8M0 scale of
+// the B operand, so O is never rescaled.  Scores are descaled by folding
+// s_Q,i * s_K,j into the exp2 constant of each tile; probabilities are
+// produced directly as P * 2^7 * mu_j (exp2 bias) and cast to E4M3, and the
+// PV instruction's block exponents supply 2^-7 (P, times the shift) and
+// 2^e_j (V), where s_V,j = mu_j * 2^e_j.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -47,6 +51,20 @@ __device__ __forceinline__ uint32_t cvt_e4m3x4(float a, float b, float c, float 
 
 __device__ __forceinline__ float clamp_e4m3(float x) { return __builtin_fminf(__builtin_fmaxf(x, -kE4M3Max), kE4M3Max); }
 
+// Value of lane L ^ B (B in 1, 2, 4, 8, inside each row of 16 lanes) through
+// DPP lane moves: quad_perm [1,0,3,2] and [2,3,0,1] give ^1 and ^2; ^4 is
+// row_half_mirror (^7) then quad_perm [3,2,1,0] (^3); ^8 is row_mirror (^15)
+// then row_half_mirror (^7).
+template <int DPP> __device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), DPP, 0xf, 0xf, true));
+}
+template <int B> __device__ __forceinline__ float lane_xor16(float x) {
+  if constexpr (B == 1) return dpp_mov<0xB1>(x);
+  else if constexpr (B == 2) return dpp_mov<0x4E>(x);
+  else if constexpr (B == 4) return dpp_mov<0x1B>(dpp_mov<0x141>(x));
+  else return dpp_mov<0x141>(dpp_mov<0x140>(x));
+}
+
 // One workgroup = 256 threads = 16 row groups x 16 lanes; a lane owns 8
 // consecutive d of 8 consecutive rows (row = 8 * group + it).
 template <int MODE>
@@ -64,6 +82,9 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8PrepParams p) {
   const uint16_t* X = p.x + (size_t)bh * p.N * D;
   const bool rot = p.signs != nullptr;
 
+  float sgn[4];  // +1 in the lower lane of each butterfly pair, -1 in the upper
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sgn[i] = (lr >> i) & 1 ? -1.f : 1.f;
   float sg[8];
   if (rot) {
     const int8_t* s8 = p.signs + h * D + lr * 8;
@@ -95,16 +116,16 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8PrepParams p) {
             y[it][e] = u + w;
             y[it][e + b] = u - w;
           }
-      // butterflies over index bits 3..6 (lanes lr ^ 1, 2, 4, 8 of the row)
+      // butterflies over index bits 3..6 (lanes lr ^ 1, 2, 4, 8 of the row):
+      // the lower lane keeps y + o, the upper one o - y, i.e. o + sgn * y
 #pragma unroll
-      for (int b = 1; b < 16; b <<= 1) {
-        const bool upper = (lr & b) != 0;
+      for (int e = 0; e < 8; ++e) y[it][e] = lane_xor16<1>(y[it][e]) + sgn[0] * y[it][e];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float o = __shfl_xor(y[it][e], b, 16);
-          y[it][e] = upper ? (o - y[it][e]) : (y[it][e] + o);
-        }
-      }
+      for (int e = 0; e < 8; ++e) y[it][e] = lane_xor16<2>(y[it][e]) + sgn[1] * y[it][e];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[it][e] = lane_xor16<4>(y[it][e]) + sgn[2] * y[it][e];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[it][e] = lane_xor16<8>(y[it][e]) + sgn[3] * y[it][e];
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(y[it][e]));
