@@ -9,9 +9,11 @@ non-causal and once causal, inputs resident in HBM.  FLOPs are counted as
 * ``roofline`` of the dominant kernel (the non-causal bf16 forward), whose
   average launch duration is measured with HIP events on the stream the
   kernel runs on, against the dense bf16 MFMA peak (2516.6 TFLOP/s);
-* ``legs``: per-kernel figures -- the d=128 sequence-length sweep at 16384
-  total tokens (TFLOPS vs N, both causal flags), the FP8 workload
-  (B4 H16 N4096 d128) prep GB/s and FP8 forward TFLOPS against the FP8 peak;
+* ``legs``: per-kernel figures -- the sequence-length sweeps at 16384 total
+  tokens for d = 128, 64 and 256 (TFLOPS and fraction of peak vs N, both
+  causal flags, plus the algorithmic HBM rate for N <= 1024), the long causal
+  context (B1 H16 N65536 d128), and the FP8 workload (B4 H16 N4096 d128):
+  prep GB/s and FP8 forward TFLOPS against the FP8 peak;
 * ``cpu_baseline``: the CPU fp64 oracle timed on a bounded sample of the
   same step on this host.
 
@@ -22,7 +24,7 @@ profiles/fwd_bf16_std_noncausal_traffic.md together with the SHA-256 of the
 kernel's sources; it is null when those sources changed since.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
-                       [--copy-calibration]
+                       [--legs sweep,sweep64,sweep256,long,fp8] [--copy-calibration]
 """
 
 from __future__ import annotations
@@ -44,6 +46,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_bf16_std_noncausal_traffic.md")
 TRAFFIC_SOURCES = ("exact_attention_73_amd/csrc/fa_fwd_bf16.hip", "exact_attention_73_amd/csrc/fa_device.h")
 COPY_CALIBRATION_BYTES = 256 << 20
+
+
+ALL_LEGS = ("sweep", "sweep64", "sweep256", "long", "fp8")
+
+
+def fwd_bytes(B, H, N, d):
+    """Algorithmic HBM bytes of one forward: bf16 Q, K, V read once, fp32 O and lse written once."""
+    return B * H * N * (3 * d * 2 + d * 4 + 4)
 
 
 def fwd_flops(B, H, N, d, causal):
@@ -103,7 +113,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--quick", action="store_true", help="skip the sweep and FP8 legs (for profiling runs)")
+    ap.add_argument("--quick", action="store_true", help="run only the timed step, no legs (for profiling runs)")
+    ap.add_argument("--legs", default=None,
+                    help=f"comma-separated legs to run after the step (default: all of {','.join(ALL_LEGS)})")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, copy 256 MiB device-to-device once, untimed, so that a "
                          "counter pass sees a kernel of known traffic beside the attention kernels")
@@ -165,43 +177,73 @@ def main():
     }
     del q, k, v
 
-    if not args.quick:
+    legs_on = set() if args.quick else set(ALL_LEGS)
+    if args.legs is not None:
+        legs_on = {x for x in args.legs.split(",") if x}
+        bad = legs_on - set(ALL_LEGS)
+        if bad:
+            raise SystemExit(f"unknown legs {sorted(bad)}; choose from {ALL_LEGS}")
+
+    for dd, name in ((128, "sweep"), (64, "sweep64"), (256, "sweep256")):
+        if name not in legs_on:
+            continue
         sweep = {}
         for sw in sweep_workloads():
-            if sw.d != 128:
+            if sw.d != dd:
                 continue
             qs, ks, vs = (x.to(dev) for x in make_qkv(sw.B, sw.H, sw.N, sw.d, sw.seed))
             row = {}
             for causal in (False, True):
                 t, _ = _time_launches(lambda: fa.fwd_bf16(qs, ks, vs, causal=causal), 20, 3)
-                row["causal" if causal else "noncausal"] = round(fwd_flops(sw.B, sw.H, sw.N, sw.d, causal) / t / 1e12, 1)
+                tf = fwd_flops(sw.B, sw.H, sw.N, sw.d, causal) / t / 1e12
+                key = "causal" if causal else "noncausal"
+                row[key] = round(tf, 1)
+                row[key + "_frac"] = round(tf / PEAK_BF16, 4)
+                if sw.N <= 1024:  # short sequences: report the algorithmic HBM rate too
+                    row[key + "_gbps"] = round(fwd_bytes(sw.B, sw.H, sw.N, sw.d) / t / 1e9, 1)
             sweep[str(sw.N)] = row
             del qs, ks, vs
-        legs["bf16_d128_sweep_tflops"] = sweep
+        legs[f"bf16_d{dd}_sweep_tflops"] = sweep
 
+    if "long" in legs_on:
+        wl = WORKLOADS["long"]
+        ql, kl, vl = (x.to(dev) for x in make_qkv(wl.B, wl.H, wl.N, wl.d, wl.seed))
+        t, _ = _time_launches(lambda: fa.fwd_bf16(ql, kl, vl, causal=True), 5, 1)
+        tf = fwd_flops(wl.B, wl.H, wl.N, wl.d, True) / t / 1e12
+        legs["bf16_long"] = {"workload": f"B{wl.B} H{wl.H} N{wl.N} d{wl.d} causal", "tflops": round(tf, 1),
+                             "frac": round(tf / PEAK_BF16, 4), "ms": round(t * 1e3, 3)}
+        del ql, kl, vl
+
+    if "fp8" in legs_on:
         w8 = WORKLOADS["fp8"]
         q, k, v = (x.to(dev) for x in make_qkv(w8.B, w8.H, w8.N, w8.d, w8.seed, outliers=True))
         signs = make_signs(w8.H, w8.d, w8.seed + 1).to(dev)
         q8, qs_ = fa.fp8_prep(q, signs=signs)
         k8, ks_ = fa.fp8_prep(k, signs=signs)
         v8t, vs_ = fa.fp8_prep_v(v)
-        t_prep, _ = _time_launches(lambda: fa.fp8_prep(q, signs=signs), 20, 3)
-        t_prep_v, _ = _time_launches(lambda: fa.fp8_prep_v(v), 20, 3)
-        t8, _ = _time_launches(lambda: fa.fwd_fp8(q8, k8, v8t, qs_, ks_, vs_), 20, 3)
+        t_prep, _ = _time_launches(lambda: fa.fp8_prep(q, signs=signs, out=q8, scale_out=qs_), 20, 3)
+        t_prep_v, _ = _time_launches(lambda: fa.fp8_prep_v(v, out=v8t, scale_out=vs_), 20, 3)
+        fa.fp8_prep(k, signs=signs, out=k8, scale_out=ks_)
+        o8 = torch.empty((w8.B, w8.H, w8.N, w8.d), dtype=torch.float32, device=dev)
+        l8 = torch.empty((w8.B, w8.H, w8.N), dtype=torch.float32, device=dev)
+        t8, _ = _time_launches(lambda: fa.fwd_fp8(q8, k8, v8t, qs_, ks_, vs_, out=o8, lse=l8), 20, 3)
+        t8c, _ = _time_launches(lambda: fa.fwd_fp8(q8, k8, v8t, qs_, ks_, vs_, causal=True, out=o8, lse=l8), 20, 3)
         elems = w8.B * w8.H * w8.N * w8.d
         prep_bytes = elems * 2 + elems + w8.B * w8.H * ((w8.N + 127) // 128) * 4
         f8 = fwd_flops(w8.B, w8.H, w8.N, w8.d, False)
-        tb, _ = _time_launches(lambda: fa.fwd_bf16(q, k, v), 20, 3)
+        tb, _ = _time_launches(lambda: fa.fwd_bf16(q, k, v, out=o8, lse=l8), 20, 3)
         legs["fp8"] = {
             "workload": "B4 H16 N4096 d128 non-causal, 0.1% N(0,10^2) outliers",
             "fwd_fp8_tflops": round(f8 / t8 / 1e12, 1),
             "fwd_fp8_frac_of_fp8_peak": round(f8 / t8 / 1e12 / PEAK_FP8, 4),
+            "fwd_fp8_causal_tflops": round(f8 / 2 / t8c / 1e12, 1),
             "fwd_bf16_same_shape_tflops": round(f8 / tb / 1e12, 1),
             "prep_qk_rotated_gbps": round(prep_bytes / t_prep / 1e9, 1),
+            "prep_qk_rotated_frac_of_hbm": round(prep_bytes / t_prep / 1e9 / PEAK_HBM, 4),
             "prep_v_transposed_gbps": round(prep_bytes / t_prep_v / 1e9, 1),
             "end_to_end_tflops": round(f8 / (t8 + 2 * t_prep + t_prep_v) / 1e12, 1),
         }
-        del q, k, v, q8, k8, v8t
+        del q, k, v, q8, k8, v8t, o8, l8
 
     if args.copy_calibration:
         src = torch.ones(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)

@@ -95,13 +95,15 @@ def fp8_vt_ld(N: int) -> int:
     return int(load().fa_fp8_vt_ld(int(N)))
 
 
-def fp8_prep(x, signs=None, transpose: bool = False, per_tensor: bool = False, pow2_scale: bool = False):
+def fp8_prep(x, signs=None, transpose: bool = False, per_tensor: bool = False, pow2_scale: bool = False,
+             out=None, scale_out=None):
     """E4M3 codes and per-128-row scales of one bf16 ``[B, H, N, d]`` tensor.
 
     ``signs``: int8 ``[H, d]`` of +-1 on the GPU (rotate, for Q and K) or None.
     For V use ``transpose=True, pow2_scale=True`` (:func:`fp8_prep_v`).
     Returns ``(x8, scale)``: uint8 ``[B, H, N, d]`` (or ``[B, H, d, ld]`` when
-    ``transpose``) and fp32 ``[B, H, ceil(N / 128)]``.
+    ``transpose``) and fp32 ``[B, H, ceil(N / 128)]``, written into ``out`` and
+    ``scale_out`` when given.
     """
     _need(x, torch.bfloat16, "x")
     B, H, N, d = x.shape
@@ -111,8 +113,12 @@ def fp8_prep(x, signs=None, transpose: bool = False, per_tensor: bool = False, p
             raise ValueError("signs must be [H, d]")
     nb = (N + 127) // 128
     shape = (B, H, d, fp8_vt_ld(N)) if transpose else (B, H, N, d)
-    x8 = torch.empty(shape, dtype=torch.uint8, device=x.device)
-    sc = torch.empty((B, H, nb), dtype=torch.float32, device=x.device)
+    x8 = torch.empty(shape, dtype=torch.uint8, device=x.device) if out is None else out
+    sc = torch.empty((B, H, nb), dtype=torch.float32, device=x.device) if scale_out is None else scale_out
+    _need(x8, torch.uint8, "out")
+    _need(sc, torch.float32, "scale_out")
+    if tuple(x8.shape) != shape or tuple(sc.shape) != (B, H, nb):
+        raise ValueError(f"out must be {shape} and scale_out {(B, H, nb)}")
     flags = ((FA_PREP_TRANSPOSE if transpose else 0) | (FA_PREP_PER_TENSOR if per_tensor else 0)
              | (FA_PREP_POW2_SCALE if pow2_scale else 0))
     st = load().fa_fp8_prep(x.data_ptr(), x8.data_ptr(), sc.data_ptr(), None if signs is None else signs.data_ptr(),
@@ -121,9 +127,9 @@ def fp8_prep(x, signs=None, transpose: bool = False, per_tensor: bool = False, p
     return x8, sc
 
 
-def fp8_prep_v(v, per_tensor: bool = False):
+def fp8_prep_v(v, per_tensor: bool = False, out=None, scale_out=None):
     """The PV operand: V transposed with power-of-two block scales."""
-    return fp8_prep(v, transpose=True, per_tensor=per_tensor, pow2_scale=True)
+    return fp8_prep(v, transpose=True, per_tensor=per_tensor, pow2_scale=True, out=out, scale_out=scale_out)
 
 
 def fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, causal: bool = False, softmax_scale: float | None = None,
