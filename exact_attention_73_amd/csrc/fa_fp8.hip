@@ -71,7 +71,10 @@ template <int MODE>
 __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8PrepParams p) {
   constexpr int D = 128;
   __shared__ float red[4];
-  __shared__ __attribute__((aligned(16))) uint8_t tr[D][128 + 16];  // transposed codes, padded rows
+  // transposed codes, one row of 128 keys per d as 32 words plus one pad
+  // word: the odd row stride spreads both the column writes and the row
+  // gathers below over the LDS banks
+  __shared__ uint32_t tr[D][33];
 
   const int nb = (p.N + 127) / 128;
   const int blk = blockIdx.x % nb;
@@ -175,7 +178,7 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8PrepParams p) {
       if (n < p.N) *reinterpret_cast<u32x2*>(Y + (size_t)n * D + lr * 8) = w;
     }
   } else {
-    // codes of d = 8 lr + e, rows 8 grp .. 8 grp + 7 -> tr[d][8 grp .. +7]
+    // codes of d = 8 lr + e, rows 8 grp .. 8 grp + 7 -> words 2 grp, 2 grp + 1 of tr[d]
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       u32x2 w;
@@ -183,7 +186,8 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8PrepParams p) {
                         clamp_e4m3(y[3][e] * inv));
       w[1] = cvt_e4m3x4(clamp_e4m3(y[4][e] * inv), clamp_e4m3(y[5][e] * inv), clamp_e4m3(y[6][e] * inv),
                         clamp_e4m3(y[7][e] * inv));
-      *reinterpret_cast<u32x2*>(&tr[lr * 8 + e][grp * 8]) = w;
+      tr[lr * 8 + e][grp * 2] = w[0];
+      tr[lr * 8 + e][grp * 2 + 1] = w[1];
     }
     __syncthreads();
     // Row d of the block: 128 keys = two 64-key segments of 16 four-key
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8PrepParams p) {
     for (int i = 0; i < 4; ++i) {
       const int ci = tid + 256 * i, d = ci >> 3, ch = ci & 7;
       const int seg = ch >> 2, w0 = (ch & 3) * 4;
-      const uint32_t* row = reinterpret_cast<const uint32_t*>(&tr[d][0]);
+      const uint32_t* row = &tr[d][0];
       u32x4 v;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
