@@ -13,7 +13,10 @@ non-causal and once causal, inputs resident in HBM.  FLOPs are counted as
   tokens for d = 128, 64 and 256 (TFLOPS and fraction of peak vs N, both
   causal flags, plus the algorithmic HBM rate for N <= 1024), the long causal
   context (B1 H16 N65536 d128), and the FP8 workload (B4 H16 N4096 d128):
-  prep GB/s and FP8 forward TFLOPS against the FP8 peak;
+  prep GB/s and FP8 forward TFLOPS against the FP8 peak.  Legs time 30
+  launches after 10 warm-ups (5 after 1 for the long context) and give the
+  mean plus the rates at the p90/median/p10 durations; N = 512 and the prep
+  kernels are also timed with cold caches (a 1 GiB write before each launch);
 * ``cpu_baseline``: the CPU fp64 oracle timed on a bounded sample of the
   same step on this host.
 
@@ -61,23 +64,55 @@ def fwd_flops(B, H, N, d, causal):
     return f / 2 if causal else f
 
 
+def _stats(ts):
+    """mean, median, p10 and p90 (seconds) of per-launch durations."""
+    ts = sorted(ts)
+    n = len(ts)
+    return {"mean": sum(ts) / n, "median": ts[n // 2], "p10": ts[int(round(0.1 * (n - 1)))],
+            "p90": ts[int(round(0.9 * (n - 1)))]}
+
+
 def _time_launches(fn, reps, warmup):
-    """Average duration (s) of fn() over reps, HIP events on the current stream."""
+    """Per-launch durations of fn() (hot caches): HIP events recorded between
+    consecutive launches on the current stream, after a device-side spin that
+    lets the host queue every launch first."""
     import torch
 
     for _ in range(warmup):
         fn()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     torch.cuda.synchronize()
-    torch.cuda._sleep(GPU_HOLD_CYCLES)  # lets the host queue every launch before the first event
+    torch.cuda._sleep(GPU_HOLD_CYCLES)
     ev[0].record()
     for i in range(reps):
         fn()
         ev[i + 1].record()
     torch.cuda.synchronize()
-    ts = [ev[i].elapsed_time(ev[i + 1]) / 1e3 for i in range(reps)]
-    ts.sort()
-    return sum(ts) / len(ts), ts[len(ts) // 2]
+    return _stats([ev[i].elapsed_time(ev[i + 1]) / 1e3 for i in range(reps)])
+
+
+def _time_cold(fn, reps, warmup, flush):
+    """Per-launch durations with cold caches: flush() (a 1 GiB write, larger
+    than the L2s and the MALL together) runs before each launch, outside the
+    event pair that brackets the launch."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e0, e1 in pairs:
+        flush()
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return _stats([e0.elapsed_time(e1) / 1e3 for e0, e1 in pairs])
+
+
+def _rates(work, st, scale):
+    """Rates at the p90, median and p10 durations (ascending), rounded."""
+    return [round(work / st[k] / scale, 1) for k in ("p90", "median", "p10")]
 
 
 def kernel_sources_sha256():
@@ -184,6 +219,14 @@ def main():
         if bad:
             raise SystemExit(f"unknown legs {sorted(bad)}; choose from {ALL_LEGS}")
 
+    scratch = None
+
+    def flush():
+        nonlocal scratch
+        if scratch is None:
+            scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        scratch.fill_(1.0)
+
     for dd, name in ((128, "sweep"), (64, "sweep64"), (256, "sweep256")):
         if name not in legs_on:
             continue
@@ -194,13 +237,21 @@ def main():
             qs, ks, vs = (x.to(dev) for x in make_qkv(sw.B, sw.H, sw.N, sw.d, sw.seed))
             row = {}
             for causal in (False, True):
-                t, _ = _time_launches(lambda: fa.fwd_bf16(qs, ks, vs, causal=causal), 20, 3)
-                tf = fwd_flops(sw.B, sw.H, sw.N, sw.d, causal) / t / 1e12
+                call = lambda: fa.fwd_bf16(qs, ks, vs, causal=causal)
+                st = _time_launches(call, 30, 10)
+                fl = fwd_flops(sw.B, sw.H, sw.N, sw.d, causal)
+                tf = fl / st["mean"] / 1e12
                 key = "causal" if causal else "noncausal"
                 row[key] = round(tf, 1)
                 row[key + "_frac"] = round(tf / PEAK_BF16, 4)
-                if sw.N <= 1024:  # short sequences: report the algorithmic HBM rate too
-                    row[key + "_gbps"] = round(fwd_bytes(sw.B, sw.H, sw.N, sw.d) / t / 1e9, 1)
+                row[key + "_p10_p50_p90"] = _rates(fl, st, 1e12)
+                if sw.N <= 1024:  # short sequences: algorithmic HBM rate, hot and cold caches
+                    by = fwd_bytes(sw.B, sw.H, sw.N, sw.d)
+                    row[key + "_gbps"] = round(by / st["mean"] / 1e9, 1)
+                    if sw.N == 512:
+                        sc = _time_cold(call, 30, 3, flush)
+                        row[key + "_cold_gbps"] = round(by / sc["mean"] / 1e9, 1)
+                        row[key + "_cold_tflops"] = round(fl / sc["mean"] / 1e12, 1)
             sweep[str(sw.N)] = row
             del qs, ks, vs
         legs[f"bf16_d{dd}_sweep_tflops"] = sweep
@@ -208,10 +259,12 @@ def main():
     if "long" in legs_on:
         wl = WORKLOADS["long"]
         ql, kl, vl = (x.to(dev) for x in make_qkv(wl.B, wl.H, wl.N, wl.d, wl.seed))
-        t, _ = _time_launches(lambda: fa.fwd_bf16(ql, kl, vl, causal=True), 5, 1)
-        tf = fwd_flops(wl.B, wl.H, wl.N, wl.d, True) / t / 1e12
+        st = _time_launches(lambda: fa.fwd_bf16(ql, kl, vl, causal=True), 5, 1)
+        fl = fwd_flops(wl.B, wl.H, wl.N, wl.d, True)
+        tf = fl / st["mean"] / 1e12
         legs["bf16_long"] = {"workload": f"B{wl.B} H{wl.H} N{wl.N} d{wl.d} causal", "tflops": round(tf, 1),
-                             "frac": round(tf / PEAK_BF16, 4), "ms": round(t * 1e3, 3)}
+                             "frac": round(tf / PEAK_BF16, 4), "ms": round(st["mean"] * 1e3, 3),
+                             "tflops_p10_p50_p90": _rates(fl, st, 1e12)}
         del ql, kl, vl
 
     if "fp8" in legs_on:
@@ -221,29 +274,37 @@ def main():
         q8, qs_ = fa.fp8_prep(q, signs=signs)
         k8, ks_ = fa.fp8_prep(k, signs=signs)
         v8t, vs_ = fa.fp8_prep_v(v)
-        t_prep, _ = _time_launches(lambda: fa.fp8_prep(q, signs=signs, out=q8, scale_out=qs_), 20, 3)
-        t_prep_v, _ = _time_launches(lambda: fa.fp8_prep_v(v, out=v8t, scale_out=vs_), 20, 3)
+        prep_q = lambda: fa.fp8_prep(q, signs=signs, out=q8, scale_out=qs_)
+        prep_v = lambda: fa.fp8_prep_v(v, out=v8t, scale_out=vs_)
+        t_prep = _time_launches(prep_q, 30, 10)
+        t_prep_v = _time_launches(prep_v, 30, 10)
+        c_prep = _time_cold(prep_q, 30, 3, flush)
+        c_prep_v = _time_cold(prep_v, 30, 3, flush)
         fa.fp8_prep(k, signs=signs, out=k8, scale_out=ks_)
         o8 = torch.empty((w8.B, w8.H, w8.N, w8.d), dtype=torch.float32, device=dev)
         l8 = torch.empty((w8.B, w8.H, w8.N), dtype=torch.float32, device=dev)
-        t8, _ = _time_launches(lambda: fa.fwd_fp8(q8, k8, v8t, qs_, ks_, vs_, out=o8, lse=l8), 20, 3)
-        t8c, _ = _time_launches(lambda: fa.fwd_fp8(q8, k8, v8t, qs_, ks_, vs_, causal=True, out=o8, lse=l8), 20, 3)
+        t8 = _time_launches(lambda: fa.fwd_fp8(q8, k8, v8t, qs_, ks_, vs_, out=o8, lse=l8), 30, 10)
+        t8c = _time_launches(lambda: fa.fwd_fp8(q8, k8, v8t, qs_, ks_, vs_, causal=True, out=o8, lse=l8), 30, 10)
         elems = w8.B * w8.H * w8.N * w8.d
         prep_bytes = elems * 2 + elems + w8.B * w8.H * ((w8.N + 127) // 128) * 4
         f8 = fwd_flops(w8.B, w8.H, w8.N, w8.d, False)
-        tb, _ = _time_launches(lambda: fa.fwd_bf16(q, k, v, out=o8, lse=l8), 20, 3)
+        tb = _time_launches(lambda: fa.fwd_bf16(q, k, v, out=o8, lse=l8), 30, 10)
         legs["fp8"] = {
             "workload": "B4 H16 N4096 d128 non-causal, 0.1% N(0,10^2) outliers",
-            "fwd_fp8_tflops": round(f8 / t8 / 1e12, 1),
-            "fwd_fp8_frac_of_fp8_peak": round(f8 / t8 / 1e12 / PEAK_FP8, 4),
-            "fwd_fp8_causal_tflops": round(f8 / 2 / t8c / 1e12, 1),
-            "fwd_bf16_same_shape_tflops": round(f8 / tb / 1e12, 1),
-            "prep_qk_rotated_gbps": round(prep_bytes / t_prep / 1e9, 1),
-            "prep_qk_rotated_frac_of_hbm": round(prep_bytes / t_prep / 1e9 / PEAK_HBM, 4),
-            "prep_v_transposed_gbps": round(prep_bytes / t_prep_v / 1e9, 1),
-            "end_to_end_tflops": round(f8 / (t8 + 2 * t_prep + t_prep_v) / 1e12, 1),
+            "fwd_fp8_tflops": round(f8 / t8["mean"] / 1e12, 1),
+            "fwd_fp8_frac_of_fp8_peak": round(f8 / t8["mean"] / 1e12 / PEAK_FP8, 4),
+            "fwd_fp8_tflops_p10_p50_p90": _rates(f8, t8, 1e12),
+            "fwd_fp8_causal_tflops": round(f8 / 2 / t8c["mean"] / 1e12, 1),
+            "fwd_bf16_same_shape_tflops": round(f8 / tb["mean"] / 1e12, 1),
+            "prep_qk_rotated_gbps": round(prep_bytes / t_prep["mean"] / 1e9, 1),
+            "prep_qk_rotated_frac_of_hbm": round(prep_bytes / t_prep["mean"] / 1e9 / PEAK_HBM, 4),
+            "prep_qk_rotated_cold_gbps": round(prep_bytes / c_prep["mean"] / 1e9, 1),
+            "prep_v_transposed_gbps": round(prep_bytes / t_prep_v["mean"] / 1e9, 1),
+            "prep_v_transposed_cold_gbps": round(prep_bytes / c_prep_v["mean"] / 1e9, 1),
+            "end_to_end_tflops": round(f8 / (t8["mean"] + 2 * t_prep["mean"] + t_prep_v["mean"]) / 1e12, 1),
         }
         del q, k, v, q8, k8, v8t, o8, l8
+    scratch = None
 
     if args.copy_calibration:
         src = torch.ones(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
@@ -276,6 +337,7 @@ def main():
             "B": B, "H": H, "N": N, "d": d, "causal": [False, True],
             "flop_convention": "4*B*H*N^2*d per forward, halved for causal",
             "device": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count,
+            "torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
             "host_wall_s": round(wall, 4),
         },
         "roofline": {

@@ -172,6 +172,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, Bf16Cfg<D>::MINB) void fwd_bf1
   constexpr int NQS = D / 16;                 // k-steps of S^T = K Q^T
   constexpr int NPS = BC / 16;                // k-steps of O^T = V^T P^T
   static_assert(INSTR % NW == 0, "tile must split over the waves");
+  static_assert(BC % 32 == 0, "key tiles are whole 32-key blocks of S^T");
 
   // one LDS object per ring slot, addressed with compile-time slot numbers,
   // so the compiler can tell the slot being filled from the slots being read
