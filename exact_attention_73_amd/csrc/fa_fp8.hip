@@ -95,16 +95,24 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8PrepParams p) {
     for (int e = 0; e < 8; ++e) sg[e] = (float)s8[e];
   }
 
+  // All eight rows are requested before any arithmetic: buffer loads with a
+  // range of N rows, so rows past N read as zero without a branch (a branch
+  // per row made each load wait for the previous one).
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), 0, p.N * D * 2, 0x00020000);
+  u32x4 raw[8];
+#pragma unroll
+  for (int it = 0; it < 8; ++it)
+    raw[it] = __builtin_amdgcn_raw_buffer_load_b128(rx, ((n0 + grp * 8 + it) * D + lr * 8) * 2, 0, 0);
+
   float y[8][8];
   float amax = 0.f;
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
-    const int n = n0 + grp * 8 + it;
-    u32x4 raw = n < p.N ? *reinterpret_cast<const u32x4*>(X + (size_t)n * D + lr * 8) : u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      y[it][2 * e] = __uint_as_float(raw[e] << 16);
-      y[it][2 * e + 1] = __uint_as_float(raw[e] & 0xffff0000u);
+      y[it][2 * e] = __uint_as_float(raw[it][e] << 16);
+      y[it][2 * e + 1] = __uint_as_float(raw[it][e] & 0xffff0000u);
     }
     if (rot) {
 #pragma unroll
@@ -166,7 +174,9 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8PrepParams p) {
   if (MODE == kPrepFused && tid == 0) p.scale[blockIdx.x] = s_out;
 
   if (!p.transpose) {
-    uint8_t* Y = p.x8 + (size_t)bh * p.N * D;
+    // codes through range-checked buffer stores: rows past N are dropped
+    const __amdgpu_buffer_rsrc_t ry =
+        __builtin_amdgcn_make_buffer_rsrc(p.x8 + (size_t)bh * p.N * D, 0, p.N * D, 0x00020000);
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int n = n0 + grp * 8 + it;
@@ -175,7 +185,7 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8PrepParams p) {
                         clamp_e4m3(y[it][3] * inv));
       w[1] = cvt_e4m3x4(clamp_e4m3(y[it][4] * inv), clamp_e4m3(y[it][5] * inv), clamp_e4m3(y[it][6] * inv),
                         clamp_e4m3(y[it][7] * inv));
-      if (n < p.N) *reinterpret_cast<u32x2*>(Y + (size_t)n * D + lr * 8) = w;
+      __builtin_amdgcn_raw_buffer_store_b64(w, ry, n * D + lr * 8, 0, 0);
     }
   } else {
     // codes of d = 8 lr + e, rows 8 grp .. 8 grp + 7 -> words 2 grp, 2 grp + 1 of tr[d]
