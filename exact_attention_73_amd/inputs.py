@@ -10,6 +10,8 @@ Recipe (CPU, deterministic; torch's Philox-free CPU generator):
   entries, which are replaced by ``10 * randn`` (N(0, 10^2)), all drawn from
   the same generator.  The pages' FP8 error study uses a synthetic
   distribution with a few large outliers without giving its parameters.
+* Upstream gradient dO (backward): ``torch.randn`` float32 ``[B, H, N, d]``
+  from ``Generator("cpu").manual_seed(seed + 2)``, cast to bfloat16.
 * Rotation signs: ``[H, d]`` int8 of +-1 from ``randint(0, 2) * 2 - 1`` with
   ``Generator("cpu").manual_seed(seed + 1)``.
 * softmax_scale = 1/sqrt(d) as a float32.
@@ -22,7 +24,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-__all__ = ["make_qkv", "make_signs", "softmax_scale", "Workload", "WORKLOADS", "sweep_workloads", "sweep_seed"]
+__all__ = ["make_qkv", "make_do", "make_signs", "softmax_scale", "Workload", "WORKLOADS", "sweep_workloads", "sweep_seed"]
 
 
 def make_qkv(B: int, H: int, N: int, d: int, seed: int, outliers: bool = False, outlier_frac: float = 1e-3,
@@ -35,6 +37,12 @@ def make_qkv(B: int, H: int, N: int, d: int, seed: int, outliers: bool = False, 
             m = torch.rand(x.shape, generator=g) < outlier_frac
             x[m] = outlier_std * torch.randn(int(m.sum()), generator=g)
     return tuple(x.to(torch.bfloat16) for x in xs)
+
+
+def make_do(B: int, H: int, N: int, d: int, seed: int) -> torch.Tensor:
+    """Upstream gradient for the backward: bf16 CPU ``[B, H, N, d]`` drawn from seed + 2."""
+    g = torch.Generator("cpu").manual_seed(int(seed) + 2)
+    return torch.randn((B, H, N, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
 
 
 def make_signs(H: int, d: int, seed: int) -> torch.Tensor:
