@@ -17,6 +17,8 @@ non-causal and once causal, inputs resident in HBM.  FLOPs are counted as
   launches after 10 warm-ups (5 after 1 for the long context) and give the
   mean plus the rates at the p90/median/p10 durations; N = 512 and the prep
   kernels are also timed with cold caches (a 1 GiB write before each launch);
+  and the backward (delta, dK/dV and dQ kernels per call) at B4 H16 N2048 and
+  N4096 d128 and N2048 d64, counted as 2.5 x the forward's FLOPs;
 * ``cpu_baseline``: the CPU fp64 oracle timed on a bounded sample of the
   same step on this host.
 
@@ -27,7 +29,7 @@ profiles/fwd_bf16_std_noncausal_traffic.md together with the SHA-256 of the
 kernel's sources; it is null when those sources changed since.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
-                       [--legs sweep,sweep64,sweep256,long,fp8] [--copy-calibration]
+                       [--legs sweep,sweep64,sweep256,long,fp8,bwd] [--copy-calibration]
 """
 
 from __future__ import annotations
@@ -51,7 +53,7 @@ TRAFFIC_SOURCES = ("exact_attention_73_amd/csrc/fa_fwd_bf16.hip", "exact_attenti
 COPY_CALIBRATION_BYTES = 256 << 20
 
 
-ALL_LEGS = ("sweep", "sweep64", "sweep256", "long", "fp8")
+ALL_LEGS = ("sweep", "sweep64", "sweep256", "long", "fp8", "bwd")
 
 
 def fwd_bytes(B, H, N, d):
@@ -163,7 +165,7 @@ def main():
     import torch
 
     import exact_attention_73_amd as fa
-    from exact_attention_73_amd.inputs import WORKLOADS, make_qkv, make_signs, softmax_scale, sweep_workloads
+    from exact_attention_73_amd.inputs import WORKLOADS, make_do, make_qkv, make_signs, softmax_scale, sweep_workloads
 
     fa.load()
     dev = torch.device("cuda:0")
@@ -305,6 +307,26 @@ def main():
         }
         del q, k, v, q8, k8, v8t, o8, l8
     scratch = None
+
+    if "bwd" in legs_on:
+        # backward: 2.5 x the forward's FLOPs (dQ, dK, dV and the recomputed
+        # S), halved for causal; the delta, dK/dV and dQ kernels in one call
+        bw = {}
+        for (Bb, Hb, Nb, db) in ((4, 16, 2048, 128), (4, 16, 4096, 128), (4, 16, 2048, 64)):
+            qb_, kb_, vb_ = (x.to(dev) for x in make_qkv(Bb, Hb, Nb, db, 73002))
+            gb_ = make_do(Bb, Hb, Nb, db, 73002).to(dev)
+            for causal in (False, True):
+                ob_, lb_ = fa.fwd_bf16(qb_, kb_, vb_, causal=causal)
+                outs = [torch.empty_like(ob_) for _ in range(3)]
+                ws = torch.empty_like(lb_)
+                st = _time_launches(lambda: fa.bwd_bf16(qb_, kb_, vb_, ob_, lb_, gb_, causal=causal, dq=outs[0],
+                                                        dk=outs[1], dv=outs[2], delta=ws), 20, 5)
+                fl = 2.5 * fwd_flops(Bb, Hb, Nb, db, causal)
+                bw[f"B{Bb} H{Hb} N{Nb} d{db} {'causal' if causal else 'non-causal'}"] = {
+                    "tflops": round(fl / st["mean"] / 1e12, 1), "frac": round(fl / st["mean"] / 1e12 / PEAK_BF16, 4),
+                    "us": round(st["mean"] * 1e6, 1), "tflops_p10_p50_p90": _rates(fl, st, 1e12)}
+            del qb_, kb_, vb_, gb_, ob_, lb_, outs, ws
+        legs["bf16_bwd"] = bw
 
     if args.copy_calibration:
         src = torch.ones(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)

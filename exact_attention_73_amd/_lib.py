@@ -25,6 +25,7 @@ FA_PREP_POW2_SCALE = 4
 _VP, _FP, _I, _F = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
 SIGNATURES = {
     "fa_fwd_bf16": (_I, [_VP, _VP, _VP, _FP, _FP, _I, _I, _I, _I, _I, _F, _VP]),
+    "fa_bwd_bf16": (_I, [_VP, _VP, _VP, _FP, _FP, _VP, _FP, _FP, _FP, _FP, _I, _I, _I, _I, _I, _F, _VP]),
     "fa_fp8_prep": (_I, [_VP, _VP, _FP, _VP, _I, _I, _I, _I, ctypes.c_uint, _VP]),
     "fa_fp8_vt_ld": (_I, [_I]),
     "fa_fwd_fp8": (_I, [_VP, _VP, _VP, _FP, _FP, _FP, _FP, _FP, _I, _I, _I, _I, _I, _F, _VP]),
@@ -93,6 +94,39 @@ def fwd_bf16(q, k, v, causal: bool = False, softmax_scale: float | None = None, 
 
 def fp8_vt_ld(N: int) -> int:
     return int(load().fa_fp8_vt_ld(int(N)))
+
+
+def bwd_bf16(q, k, v, o, lse, dout, causal: bool = False, softmax_scale: float | None = None, dq=None, dk=None,
+             dv=None, delta=None):
+    """dQ, dK, dV (fp32 ``[B, H, N, d]``) of the forward for the upstream
+    gradient ``dout`` (bf16), from the forward's ``o`` and ``lse`` (fp32).
+    ``delta`` is the fp32 ``[B, H, N]`` workspace (allocated when omitted)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _need(t, torch.bfloat16, n)
+    _need(o, torch.float32, "o")
+    _need(lse, torch.float32, "lse")
+    if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, dout, o)):
+        raise ValueError("q, k, v, dout, o must share one shape [B, H, N, d]")
+    B, H, N, d = q.shape
+    if tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be [B, H, N]")
+    scale = (1.0 / d ** 0.5) if softmax_scale is None else float(softmax_scale)
+    outs = []
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        t = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if t is None else t
+        _need(t, torch.float32, n)
+        if tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"{n} must be [B, H, N, d]")
+        outs.append(t)
+    ws = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
+    _need(ws, torch.float32, "delta")
+    if tuple(ws.shape) != (B, H, N):
+        raise ValueError("delta must be [B, H, N]")
+    st = load().fa_bwd_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                            outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(), ws.data_ptr(), B, H, N, d,
+                            int(bool(causal)), scale, _stream(q))
+    _check("fa_bwd_bf16", st)
+    return tuple(outs)
 
 
 def fp8_prep(x, signs=None, transpose: bool = False, per_tensor: bool = False, pow2_scale: bool = False,

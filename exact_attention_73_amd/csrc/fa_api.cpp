@@ -104,6 +104,40 @@ int fa_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* ls
   return launch_status(fa::launch_fwd_bf16(p, d, causal == 1, static_cast<hipStream_t>(stream)));
 }
 
+int fa_bwd_bf16(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
+                float* dq, float* dk, float* dv, float* delta_ws, int B, int H, int N, int d, int causal,
+                float softmax_scale, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta_ws) return FA_ERR_NULL_PTR;
+  if (int e = check_shape(B, H, N, d == 64 || d == 128 ? d : 1)) return e;
+  // fp32 [N, d] slices are addressed with 32-bit byte offsets too
+  if ((double)N * (double)d * 4.0 >= 2147483648.0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (int e = check_scale(softmax_scale)) return e;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(delta_ws))
+    return FA_ERR_ALIGN;
+  if (int e = check_device()) return e;
+
+  fa::BwdBf16Params p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.o = o;
+  p.lse = lse;
+  p.delta = delta_ws;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.scale = softmax_scale;
+  p.c = softmax_scale * 1.4426950408889634f;
+  return launch_status(fa::launch_bwd_bf16(p, d, causal == 1, static_cast<hipStream_t>(stream)));
+}
+
 int fa_fp8_prep(const void* x, void* x8, float* x_scale, const signed char* signs, int B, int H, int N, int d,
                 unsigned flags, void* stream) {
   if (!x || !x8 || !x_scale) return FA_ERR_NULL_PTR;

@@ -21,6 +21,24 @@ struct FwdBf16Params {
 
 hipError_t launch_fwd_bf16(const FwdBf16Params& p, int d, bool causal, hipStream_t stream);
 
+struct BwdBf16Params {
+  const uint16_t* q;     // bf16 [B, H, N, d]
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;  // bf16 [B, H, N, d], upstream gradient
+  const float* o;        // fp32 [B, H, N, d], forward output
+  const float* lse;      // fp32 [B, H, N], forward logsumexp (natural log)
+  float* delta;          // fp32 [B, H, N] workspace: rowsum(dO * O)
+  float* dq;             // fp32 [B, H, N, d]
+  float* dk;
+  float* dv;
+  int B, H, N;
+  float scale;  // softmax scale
+  float c;      // scale * log2(e)
+};
+
+hipError_t launch_bwd_bf16(const BwdBf16Params& p, int d, bool causal, hipStream_t stream);
+
 struct Fp8PrepParams {
   const uint16_t* x;   // bf16 [B, H, N, d]
   uint8_t* x8;         // E4M3 codes, [B, H, N, d] or [B, H, d, ld]

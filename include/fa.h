@@ -75,6 +75,31 @@ int fa_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* ls
                 int causal, float softmax_scale, void* stream);
 
 /*
+ * fa_bwd_bf16 -- exact attention backward: dQ, dK, dV of the forward above
+ * for an upstream gradient dO, recomputing P from the saved logsumexp
+ * (the derivative of the forward's definition, wmrh.cn FlashAttention V3
+ * article, section 一.1; the FA3 explainer lists dQ, dK, dV among what a
+ * correctness suite must cover, section "正确性验证要覆盖异步边界"):
+ *   D = rowsum(dO * O), dV = P^T dO, dS = P * (dO V^T - D),
+ *   dQ = scale dS K, dK = scale dS^T Q.
+ *
+ *   q, k, v, dout : bf16 [B, H, N, d]   (read only; the forward's inputs)
+ *   o             : fp32 [B, H, N, d]   (read only; the forward's output)
+ *   lse           : fp32 [B, H, N]      (read only; the forward's logsumexp)
+ *   dq, dk, dv    : fp32 [B, H, N, d]   (every element written)
+ *   delta_ws      : fp32 [B, H, N]      caller-owned workspace, overwritten
+ *                                       with D (the library allocates nothing)
+ *   d             : 64 or 128           (FA_ERR_HEADDIM otherwise)
+ *   causal, softmax_scale : as for the forward, and equal to its values.
+ *
+ * Also FA_ERR_SHAPE when N * d * 4 >= 2^31.  Three kernels run in order on
+ * `stream`: D, then dK/dV, then dQ; no atomics, so results are deterministic.
+ */
+int fa_bwd_bf16(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
+                float* dq, float* dk, float* dv, float* delta_ws, int B, int H, int N, int d, int causal,
+                float softmax_scale, void* stream);
+
+/*
  * fa_fp8_prep -- one pass over one tensor that produces the FP8 operands of
  * fa_fwd_fp8 ("Incoherent Processing" and "Block Quantization" sections of
  * the FA3 explainer cited above; E4M3 largest value 448 from the wmrh.cn

@@ -12,11 +12,15 @@ def errors(got, ref):
     d = got - ref
     rmse = float(np.sqrt(np.mean(d * d))) if d.size else 0.0
     rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
-    cos = float((got * ref).sum() / np.sqrt((got * got).sum() * (ref * ref).sum())) if ref.size else 1.0
+    nn = float(np.sqrt((got * got).sum() * (ref * ref).sum())) if ref.size else 0.0
+    if nn > 0:
+        cos = float((got * ref).sum() / nn)
+    else:  # an all-zero side: agreement only if both are zero
+        cos = 1.0 if rmse == 0.0 else 0.0
     return {
         "max_abs": float(np.abs(d).max()) if d.size else 0.0,
         "rmse": rmse,
-        "rel_rmse": rmse / rms if rms > 0 else 0.0,
+        "rel_rmse": rmse / rms if rms > 0 else (0.0 if rmse == 0.0 else float("inf")),
         "cos": cos,
     }
 

@@ -73,6 +73,17 @@ def test_fp8_validation(lib):
     assert p(flags=4, signs=FAKE) == -4  # power-of-two scales are for the unrotated V operand
 
 
+def test_bwd_validation(lib):
+    f = lambda **kw: lib.fa_bwd_bf16(kw.get("q", FAKE), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     kw.get("ws", FAKE), kw.get("B", 1), 1, kw.get("N", 64), kw.get("d", 128),
+                                     kw.get("causal", 0), kw.get("scale", 0.1), None)
+    assert f(q=None) == -1 and f(ws=None) == -1
+    assert f(B=0) == -2 and f(N=1 << 22) == -2  # N * d * 4 >= 2^31
+    assert f(d=256) == -3 and f(d=32) == -3
+    assert f(causal=3) == -4 and f(scale=0.0) == -4
+    assert f(ws=FAKE + 4) == -5
+
+
 def test_valid_call_without_gpu_reports_device_error(lib):
     import torch
 
