@@ -20,6 +20,8 @@ Modules:
 
 * :mod:`oracle.attention` -- ``attention_ref`` (the plain definition, S
   materialised) and ``online_ref`` (the tiled online-softmax recurrence).
+* :mod:`oracle.gqa` -- ``attention_gqa_ref`` (grouped/multi-query heads,
+  unequal query and key lengths, bottom-right causal alignment).
 * :mod:`oracle.backward` -- ``attention_bwd_ref`` (dQ, dK, dV of the
   definition, written out).
 * :mod:`oracle.fp8` -- OCP E4M3 codec, Sylvester Hadamard rotation, per-block
@@ -34,6 +36,7 @@ marked "parity unpinned" in :mod:`oracle.fp8`.
 
 from .attention import attention_ref, online_ref  # noqa: F401
 from .backward import attention_bwd_ref  # noqa: F401
+from .gqa import attention_gqa_ref  # noqa: F401
 from .fp8 import (  # noqa: F401
     E4M3_MAX,
     e4m3_decode,
