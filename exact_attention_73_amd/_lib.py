@@ -25,6 +25,7 @@ FA_PREP_POW2_SCALE = 4
 _VP, _FP, _I, _F = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
 SIGNATURES = {
     "fa_fwd_bf16": (_I, [_VP, _VP, _VP, _FP, _FP, _I, _I, _I, _I, _I, _F, _VP]),
+    "fa_fwd_bf16_gqa": (_I, [_VP, _VP, _VP, _FP, _FP, _I, _I, _I, _I, _I, _I, _I, _F, _VP]),
     "fa_bwd_bf16": (_I, [_VP, _VP, _VP, _FP, _FP, _VP, _FP, _FP, _FP, _FP, _I, _I, _I, _I, _I, _F, _VP]),
     "fa_fp8_prep": (_I, [_VP, _VP, _FP, _VP, _I, _I, _I, _I, ctypes.c_uint, _VP]),
     "fa_fp8_vt_ld": (_I, [_I]),
@@ -94,6 +95,26 @@ def fwd_bf16(q, k, v, causal: bool = False, softmax_scale: float | None = None, 
 
 def fp8_vt_ld(N: int) -> int:
     return int(load().fa_fp8_vt_ld(int(N)))
+
+
+def fwd_bf16_gqa(q, k, v, causal: bool = False, softmax_scale: float | None = None, out=None, lse=None):
+    """Forward for q ``[B, Hq, Nq, d]`` and k, v ``[B, Hkv, Nk, d]`` (bf16);
+    bottom-right causal alignment. Returns fp32 ``o [B, Hq, Nq, d]``, ``lse [B, Hq, Nq]``."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, n)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError("q must be [B, Hq, Nq, d] and k, v [B, Hkv, Nk, d]")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    scale = (1.0 / d ** 0.5) if softmax_scale is None else float(softmax_scale)
+    o = torch.empty((B, Hq, Nq, d), dtype=torch.float32, device=q.device) if out is None else out
+    ls = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(o, torch.float32, "out")
+    _need(ls, torch.float32, "lse")
+    st = load().fa_fwd_bf16_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), ls.data_ptr(), B, Hq, Hkv,
+                                Nq, Nk, d, int(bool(causal)), scale, _stream(q))
+    _check("fa_fwd_bf16_gqa", st)
+    return o, ls
 
 
 def bwd_bf16(q, k, v, o, lse, dout, causal: bool = False, softmax_scale: float | None = None, dq=None, dk=None,

@@ -99,6 +99,38 @@ int fa_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* ls
   p.B = B;
   p.H = H;
   p.N = N;
+  p.Hkv = H;
+  p.Nk = N;
+  p.scale = softmax_scale;
+  p.c = softmax_scale * 1.4426950408889634f;
+  return launch_status(fa::launch_fwd_bf16(p, d, causal == 1, static_cast<hipStream_t>(stream)));
+}
+
+int fa_fwd_bf16_gqa(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Hq, int Hkv,
+                    int Nq, int Nk, int d, int causal, float softmax_scale, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_PTR;
+  const int dd = d == 64 || d == 128 || d == 256 ? d : 1;
+  if (Hkv < 1 || Nk < 1) return FA_ERR_SHAPE;
+  if (int e = check_shape(B, Hq, Nq, dd)) return e;
+  if (int e = check_shape(B, Hkv, Nk, dd)) return e;
+  if (Hq % Hkv) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_HEADDIM;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (int e = check_scale(softmax_scale)) return e;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  if (int e = check_device()) return e;
+
+  fa::FwdBf16Params p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.H = Hq;
+  p.N = Nq;
+  p.Hkv = Hkv;
+  p.Nk = Nk;
   p.scale = softmax_scale;
   p.c = softmax_scale * 1.4426950408889634f;
   return launch_status(fa::launch_fwd_bf16(p, d, causal == 1, static_cast<hipStream_t>(stream)));

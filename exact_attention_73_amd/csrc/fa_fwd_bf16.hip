@@ -181,7 +181,9 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, Bf16Cfg<D>::MINB) void fwd_bf1
   __shared__ __attribute__((aligned(1024))) uint16_t Vs0[BC * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Vs1[BC * D];
 
-  const int N = p.N;
+  const int N = p.N;    // queries
+  const int Nk = p.Nk;  // keys
+  const int off = Nk - N;  // causal alignment: query i sees keys j <= i + off
   const int BH = p.B * p.H;
   const int nq = (N + BR - 1) / BR;
   int bh, qt;
@@ -197,7 +199,10 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, Bf16Cfg<D>::MINB) void fwd_bf1
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const size_t base = (size_t)bh * N * D;
+  const size_t base = (size_t)bh * N * D;  // q, o
+  // KV head of this query head: each KV head serves H / Hkv consecutive query heads
+  const int bb = bh / p.H, hh = bh - bb * p.H;
+  const size_t kvbase = ((size_t)bb * p.Hkv + hh / (p.H / p.Hkv)) * Nk * D;
   const int q0 = qt * BR + wave * QW;  // first query row of this wave
   int qrow[QB];                        // the query rows this lane owns
 #pragma unroll
@@ -217,15 +222,15 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, Bf16Cfg<D>::MINB) void fwd_bf1
     }
   }
 
-  const int kend = CAUSAL ? min(N, qt * BR + BR) : N;
-  const int ntiles = (kend + BC - 1) / BC;
+  const int kend = CAUSAL ? min(Nk, qt * BR + BR + off) : Nk;
+  const int ntiles = kend > 0 ? (kend + BC - 1) / BC : 0;
 
   // ---- direct-to-LDS tile loads -------------------------------------------
   // Wave-load i of wave w fills LDS bytes [(IPW w + i) KB, +1 KB) of the
   // slot: RPI rows; lane L writes physical chunk L % CPR of row L / CPR and
   // therefore fetches the logical chunk that the swizzle puts there.
-  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(p.k + base, N * ROWB);
-  const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(p.v + base, N * ROWB);
+  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(p.k + kvbase, Nk * ROWB);
+  const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(p.v + kvbase, Nk * ROWB);
   int koff[IPW], voff[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
@@ -303,10 +308,10 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, Bf16Cfg<D>::MINB) void fwd_bf1
     if (j + 2 < ntiles) issue(rk, k_this, koff, j + 2);
     if (j + 1 < ntiles) issue(rv, v_next, voff, j + 1);
     const int key0 = j * BC;
-    if (CAUSAL && key0 > q0 + QW - 1) return;  // every row of this wave lies above tile j (and all later ones)
+    if (CAUSAL && key0 > q0 + QW - 1 + off) return;  // every row of this wave lies above tile j (and all later ones)
 
     // ---- mask (only tiles crossing the diagonal or the end of N) ----------
-    const bool need_mask = (CAUSAL && key0 + BC - 1 > q0) || (key0 + BC > N);
+    const bool need_mask = (CAUSAL && key0 + BC - 1 > q0 + off) || (key0 + BC > Nk);
     if (need_mask) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -315,7 +320,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, Bf16Cfg<D>::MINB) void fwd_bf1
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const bool dead = (CAUSAL && key > qrow[qb]) || key >= N;
+            const bool dead = (CAUSAL && key > qrow[qb] + off) || key >= Nk;
             s_in[qb][kb][r] = dead ? -INFINITY : s_in[qb][kb][r];
           }
         mx[qb] = rowmax(s_in[qb]);
@@ -329,7 +334,9 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, Bf16Cfg<D>::MINB) void fwd_bf1
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const float m_new = __builtin_fmaxf(m_run[qb], mx[qb]);
-        const float alpha = exp2_fast((m_run[qb] - m_new) * c);  // 0 on the first tile
+        // 0 on a row's first visible tile; a row that has seen no key yet
+        // (m_new = -inf, l = 0, O = 0) must not take (-inf) - (-inf) = NaN
+        const float alpha = m_new == -INFINITY ? 1.f : exp2_fast((m_run[qb] - m_new) * c);
         l_run[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[qb][db] *= alpha;
@@ -383,8 +390,10 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, Bf16Cfg<D>::MINB) void fwd_bf1
   // ---- prologue: K_0, V_0, K_1 in flight; S_0 and its row max ---------------
   f32x16 sa[QB][NKB], sb[QB][NKB];
   float mx[QB];
-  issue(rk, Ks0, koff, 0);
-  issue(rv, Vs0, voff, 0);
+  if (ntiles > 0) {
+    issue(rk, Ks0, koff, 0);
+    issue(rv, Vs0, voff, 0);
+  }
   if (ntiles > 1) issue(rk, Ks1, koff, 1);
   wait_vmem_all();
   __syncthreads();
@@ -401,7 +410,8 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, Bf16Cfg<D>::MINB) void fwd_bf1
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = l_run[qb] + swap_halves(l_run[qb]);
     if (qrow[qb] < N) {
-      const float inv = 1.f / l_tot;
+      // a row that sees no key (only when N > Nk, causal) has l = 0: O = 0, lse = -inf
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       float* orow = p.o + base + (size_t)qrow[qb] * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)

@@ -10,11 +10,12 @@ namespace fa {
 
 struct FwdBf16Params {
   const uint16_t* q;  // bf16 [B, H, N, d]
-  const uint16_t* k;
+  const uint16_t* k;  // bf16 [B, Hkv, Nk, d]
   const uint16_t* v;
   float* o;    // fp32 [B, H, N, d]
   float* lse;  // fp32 [B, H, N]
   int B, H, N;
+  int Hkv, Nk;   // KV heads (H a multiple of Hkv) and keys; query i sees keys j <= i + Nk - N when causal
   float scale;   // softmax scale
   float c;       // scale * log2(e)
 };

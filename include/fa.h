@@ -75,6 +75,26 @@ int fa_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* ls
                 int causal, float softmax_scale, void* stream);
 
 /*
+ * fa_fwd_bf16_gqa -- the same forward for grouped- and multi-query heads
+ * and unequal query / key lengths (the FA3 explainer names grouped and
+ * multi-query KV heads and short queries against long keys among the shapes
+ * a kernel meets, section "为什么 Causal Shape 可能更难调度", and lists
+ * "Q/K 不同长度" among what tests must cover, section "正确性验证要覆盖异步边界").
+ *
+ *   q    : bf16 [B, Hq, Nq, d]      k, v : bf16 [B, Hkv, Nk, d]   (read only)
+ *   o    : fp32 [B, Hq, Nq, d]      lse  : fp32 [B, Hq, Nq]       (every element written)
+ *   Hq   : a multiple of Hkv; query head h reads KV head h / (Hq / Hkv)
+ *   causal : 1 = bottom-right alignment, query i sees keys j <= i + Nk - Nq
+ *            (a single query sees every key; Nq = Nk is fa_fwd_bf16's mask).
+ *            A query that sees no key (Nq > Nk) gets o = 0 and lse = -inf.
+ *   d, softmax_scale : as fa_fwd_bf16.
+ *
+ * FA_ERR_SHAPE also when Hkv < 1, Nk < 1 or Hq % Hkv != 0.
+ */
+int fa_fwd_bf16_gqa(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Hq, int Hkv,
+                    int Nq, int Nk, int d, int causal, float softmax_scale, void* stream);
+
+/*
  * fa_bwd_bf16 -- exact attention backward: dQ, dK, dV of the forward above
  * for an upstream gradient dO, recomputing P from the saved logsumexp
  * (the derivative of the forward's definition, wmrh.cn FlashAttention V3

@@ -73,6 +73,15 @@ def test_fp8_validation(lib):
     assert p(flags=4, signs=FAKE) == -4  # power-of-two scales are for the unrotated V operand
 
 
+def test_gqa_validation(lib):
+    f = lambda **kw: lib.fa_fwd_bf16_gqa(kw.get("q", FAKE), FAKE, FAKE, FAKE, FAKE, 1, kw.get("Hq", 8),
+                                         kw.get("Hkv", 2), kw.get("Nq", 16), kw.get("Nk", 64), kw.get("d", 128),
+                                         kw.get("causal", 0), 0.1, None)
+    assert f(q=None) == -1
+    assert f(Hkv=0) == -2 and f(Nk=0) == -2 and f(Hq=6, Hkv=4) == -2 and f(Nq=0) == -2
+    assert f(d=96) == -3 and f(causal=2) == -4
+
+
 def test_bwd_validation(lib):
     f = lambda **kw: lib.fa_bwd_bf16(kw.get("q", FAKE), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                      kw.get("ws", FAKE), kw.get("B", 1), 1, kw.get("N", 64), kw.get("d", 128),

@@ -1,0 +1,67 @@
+"""GPU parity of fa_fwd_bf16_gqa (grouped/multi-query heads, unequal query
+and key lengths, bottom-right causal) against the fp64 oracle; same gates
+as the square forward (max-abs <= 1e-2, RMSE <= 2e-3, relative RMSE <= 1e-2,
+lse <= 1e-3 on rows that see keys; o = 0 and lse = -inf on rows that see
+none)."""
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_73_amd as fa
+from exact_attention_73_amd.inputs import make_qkv, softmax_scale
+from oracle import attention_gqa_ref
+from tests._util import errors
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(B, Hq, Hkv, Nq, Nk, d, seed):
+    q, _, _ = make_qkv(B, Hq, Nq, d, seed)
+    _, k, v = make_qkv(B, Hkv, Nk, d, seed + 1)
+    return q, k, v
+
+
+def _check(B, Hq, Hkv, Nq, Nk, d, causal, seed):
+    q, k, v = _inputs(B, Hq, Hkv, Nq, Nk, d, seed)
+    o, lse = fa.fwd_bf16_gqa(q.cuda(), k.cuda(), v.cuda(), causal=causal)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    o_ref, lse_ref = attention_gqa_ref(q, k, v, causal=causal, scale=softmax_scale(d))
+    seen = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse), seen)
+    assert np.all(o[~seen] == 0) and np.all(np.isneginf(lse[~seen]))
+    e = errors(o[seen], o_ref[seen])
+    print(f"Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} causal={causal}: {e}")
+    assert e["max_abs"] <= 1e-2 and e["rmse"] <= 2e-3 and e["rel_rmse"] <= 1e-2, e
+    if seen.any():
+        assert float(np.abs(lse[seen] - lse_ref[seen]).max()) <= 1e-3
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (6, 1)])
+@pytest.mark.parametrize("Nq,Nk", [(1, 1000), (7, 300), (128, 129), (200, 64), (300, 700), (513, 513)])
+def test_gqa_shapes(Nq, Nk, Hq, Hkv, d, causal):
+    _check(1, Hq, Hkv, Nq, Nk, d, causal, seed=7000 + Nq + Nk + d)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_decode_batch(causal):
+    # decode-like: a few queries per head against a long cache, several batches
+    _check(4, 16, 2, 4, 4096, 128, causal, seed=7100)
+
+
+def test_gqa_equals_square_forward_when_groups_are_one():
+    q, k, v = make_qkv(2, 4, 333, 128, seed=7200)
+    a = fa.fwd_bf16_gqa(q.cuda(), k.cuda(), v.cuda(), causal=True)
+    b = fa.fwd_bf16(q.cuda(), k.cuda(), v.cuda(), causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_gqa_invalid_arguments():
+    q, k, v = _inputs(1, 6, 4, 64, 64, 128, seed=1)
+    with pytest.raises(fa.FaError) as ei:
+        fa.fwd_bf16_gqa(q.cuda(), k.cuda(), v.cuda())
+    assert ei.value.status == -2  # 6 query heads do not group over 4 KV heads
