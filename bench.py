@@ -53,12 +53,18 @@ TRAFFIC_SOURCES = ("exact_attention_73_amd/csrc/fa_fwd_bf16.hip", "exact_attenti
 COPY_CALIBRATION_BYTES = 256 << 20
 
 
-ALL_LEGS = ("sweep", "sweep64", "sweep256", "long", "fp8", "bwd")
+ALL_LEGS = ("sweep", "sweep64", "sweep256", "long", "fp8", "bwd", "decode")
 
 
 def fwd_bytes(B, H, N, d):
     """Algorithmic HBM bytes of one forward: bf16 Q, K, V read once, fp32 O and lse written once."""
     return B * H * N * (3 * d * 2 + d * 4 + 4)
+
+
+def decode_bytes(B, Hq, Hkv, Nq, Nk, d):
+    """Algorithmic HBM bytes of one decode forward: bf16 K and V read once
+    per KV head, bf16 Q read once, fp32 O and lse written once."""
+    return B * Hkv * Nk * d * 2 * 2 + B * Hq * Nq * (d * 2 + d * 4 + 4)
 
 
 def fwd_flops(B, H, N, d, causal):
@@ -327,6 +333,38 @@ def main():
                     "us": round(st["mean"] * 1e6, 1), "tflops_p10_p50_p90": _rates(fl, st, 1e12)}
             del qb_, kb_, vb_, gb_, ob_, lb_, outs, ws
         legs["bf16_bwd"] = bw
+
+    if "decode" in legs_on:
+        # few queries against long keys: HBM-bound on the K/V read.  The split
+        # count is the library's choice; the prefill-shaped kernel on the same
+        # shape is timed beside it.
+        dec = {}
+        for (Bd, Hq, Hkv, Nq, Nk, dd) in ((16, 32, 8, 1, 8192, 128), (1, 32, 8, 1, 131072, 128),
+                                           (8, 32, 32, 1, 8192, 128), (16, 32, 8, 4, 8192, 128),
+                                           (32, 16, 2, 1, 8192, 64), (16, 16, 4, 1, 8192, 256)):
+            qd_, _, _ = make_qkv(Bd, Hq, Nq, dd, 73600)
+            _, kd_, vd_ = make_qkv(Bd, Hkv, Nk, dd, 73601)
+            qd_, kd_, vd_ = qd_.to(dev), kd_.to(dev), vd_.to(dev)
+            od_ = torch.empty((Bd, Hq, Nq, dd), dtype=torch.float32, device=dev)
+            ld_ = torch.empty((Bd, Hq, Nq), dtype=torch.float32, device=dev)
+            splits = fa.decode_splits(Bd, Hq, Hkv, Nq, Nk, dd)
+            need = fa.decode_workspace_bytes(Bd, Hq, Nq, dd, splits)
+            wsd = torch.empty(max(need // 4, 1), dtype=torch.float32, device=dev)
+            call = lambda: fa.fwd_bf16_decode(qd_, kd_, vd_, causal=True, num_splits=splits, out=od_, lse=ld_,
+                                              workspace=wsd)
+            st = _time_launches(call, 30, 10)
+            sc = _time_cold(call, 30, 3, flush)
+            sp = _time_launches(lambda: fa.fwd_bf16_gqa(qd_, kd_, vd_, causal=True, out=od_, lse=ld_), 10, 3)
+            by = decode_bytes(Bd, Hq, Hkv, Nq, Nk, dd)
+            dec[f"B{Bd} Hq{Hq} Hkv{Hkv} Nq{Nq} Nk{Nk} d{dd} causal"] = {
+                "splits": splits, "us": round(st["mean"] * 1e6, 1), "gbps": round(by / st["mean"] / 1e9, 1),
+                "frac_of_hbm": round(by / st["mean"] / 1e9 / PEAK_HBM, 4),
+                "cold_us": round(sc["mean"] * 1e6, 1), "cold_gbps": round(by / sc["mean"] / 1e9, 1),
+                "cold_frac_of_hbm": round(by / sc["mean"] / 1e9 / PEAK_HBM, 4),
+                "gbps_p10_p50_p90": _rates(by, st, 1e9),
+                "prefill_kernel_same_shape_us": round(sp["mean"] * 1e6, 1)}
+            del qd_, kd_, vd_, od_, ld_, wsd
+        legs["bf16_decode"] = dec
 
     if args.copy_calibration:
         src = torch.ones(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)

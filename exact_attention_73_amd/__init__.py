@@ -5,6 +5,20 @@ The compute lives in hand-written HIP kernels behind the C ABI of
 here only marshal torch tensors into that ABI.
 """
 
-from ._lib import FaError, bwd_bf16, fp8_prep, fp8_prep_v, fp8_vt_ld, fwd_bf16, fwd_bf16_gqa, fwd_fp8, load  # noqa: F401
+from ._lib import (  # noqa: F401
+    FaError,
+    bwd_bf16,
+    decode_splits,
+    decode_workspace_bytes,
+    fp8_prep,
+    fp8_prep_v,
+    fp8_vt_ld,
+    fwd_bf16,
+    fwd_bf16_decode,
+    fwd_bf16_gqa,
+    fwd_fp8,
+    load,
+)
 
-__all__ = ["fwd_bf16", "fwd_bf16_gqa", "bwd_bf16", "fp8_prep", "fp8_prep_v", "fwd_fp8", "fp8_vt_ld", "load", "FaError"]
+__all__ = ["fwd_bf16", "fwd_bf16_gqa", "fwd_bf16_decode", "decode_splits", "decode_workspace_bytes",
+           "bwd_bf16", "fp8_prep", "fp8_prep_v", "fwd_fp8", "fp8_vt_ld", "load", "FaError"]

@@ -22,10 +22,13 @@ FA_PREP_PER_TENSOR = 2
 FA_PREP_POW2_SCALE = 4
 
 # every function the header declares, with its ctypes signature
-_VP, _FP, _I, _F = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+_VP, _FP, _I, _F, _LL = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_longlong
 SIGNATURES = {
     "fa_fwd_bf16": (_I, [_VP, _VP, _VP, _FP, _FP, _I, _I, _I, _I, _I, _F, _VP]),
     "fa_fwd_bf16_gqa": (_I, [_VP, _VP, _VP, _FP, _FP, _I, _I, _I, _I, _I, _I, _I, _F, _VP]),
+    "fa_fwd_bf16_decode_splits": (_I, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "fa_fwd_bf16_decode_workspace": (_LL, [_I, _I, _I, _I, _I]),
+    "fa_fwd_bf16_decode": (_I, [_VP, _VP, _VP, _FP, _FP, _I, _I, _I, _I, _I, _I, _I, _F, _I, _VP, _LL, _VP]),
     "fa_bwd_bf16": (_I, [_VP, _VP, _VP, _FP, _FP, _VP, _FP, _FP, _FP, _FP, _I, _I, _I, _I, _I, _F, _VP]),
     "fa_fp8_prep": (_I, [_VP, _VP, _FP, _VP, _I, _I, _I, _I, ctypes.c_uint, _VP]),
     "fa_fp8_vt_ld": (_I, [_I]),
@@ -100,12 +103,7 @@ def fp8_vt_ld(N: int) -> int:
 def fwd_bf16_gqa(q, k, v, causal: bool = False, softmax_scale: float | None = None, out=None, lse=None):
     """Forward for q ``[B, Hq, Nq, d]`` and k, v ``[B, Hkv, Nk, d]`` (bf16);
     bottom-right causal alignment. Returns fp32 ``o [B, Hq, Nq, d]``, ``lse [B, Hq, Nq]``."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, torch.bfloat16, n)
-    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
-        raise ValueError("q must be [B, Hq, Nq, d] and k, v [B, Hkv, Nk, d]")
-    B, Hq, Nq, d = q.shape
-    Hkv, Nk = k.shape[1], k.shape[2]
+    B, Hq, Hkv, Nq, Nk, d = _gqa_shapes(q, k, v)
     scale = (1.0 / d ** 0.5) if softmax_scale is None else float(softmax_scale)
     o = torch.empty((B, Hq, Nq, d), dtype=torch.float32, device=q.device) if out is None else out
     ls = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
@@ -114,6 +112,62 @@ def fwd_bf16_gqa(q, k, v, causal: bool = False, softmax_scale: float | None = No
     st = load().fa_fwd_bf16_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), ls.data_ptr(), B, Hq, Hkv,
                                 Nq, Nk, d, int(bool(causal)), scale, _stream(q))
     _check("fa_fwd_bf16_gqa", st)
+    return o, ls
+
+
+def _gqa_shapes(q, k, v):
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, n)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError("q must be [B, Hq, Nq, d] and k, v [B, Hkv, Nk, d]")
+    B, Hq, Nq, d = q.shape
+    return B, Hq, k.shape[1], Nq, k.shape[2], d
+
+
+def decode_splits(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, num_splits: int = 0,
+                  num_cus: int | None = None) -> int:
+    """Key chunks per KV head that ``fwd_bf16_decode`` uses (0 = the cost
+    model's choice for ``num_cus`` compute units, default: the current GPU's)."""
+    if num_cus is None:
+        num_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    s = load().fa_fwd_bf16_decode_splits(B, Hq, Hkv, Nq, Nk, d, int(num_splits), int(num_cus))
+    if s < 0:
+        _check("fa_fwd_bf16_decode_splits", s)
+    return s
+
+
+def decode_workspace_bytes(B: int, Hq: int, Nq: int, d: int, splits: int) -> int:
+    n = load().fa_fwd_bf16_decode_workspace(B, Hq, Nq, d, splits)
+    if n < 0:
+        _check("fa_fwd_bf16_decode_workspace", int(n))
+    return int(n)
+
+
+def fwd_bf16_decode(q, k, v, causal: bool = False, softmax_scale: float | None = None, num_splits: int = 0,
+                    out=None, lse=None, workspace=None):
+    """Split-KV forward for few queries against long keys: q ``[B, Hq, Nq, d]``,
+    k, v ``[B, Hkv, Nk, d]`` (bf16); same result as ``fwd_bf16_gqa``.
+    ``num_splits`` 0 lets the library choose; ``workspace`` (any dtype,
+    contiguous, on the GPU) is allocated when omitted and needed."""
+    B, Hq, Hkv, Nq, Nk, d = _gqa_shapes(q, k, v)
+    scale = (1.0 / d ** 0.5) if softmax_scale is None else float(softmax_scale)
+    cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+    splits = decode_splits(B, Hq, Hkv, Nq, Nk, d, num_splits, cus)
+    need = decode_workspace_bytes(B, Hq, Nq, d, splits)
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on a GPU")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    o = torch.empty((B, Hq, Nq, d), dtype=torch.float32, device=q.device) if out is None else out
+    ls = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(o, torch.float32, "out")
+    _need(ls, torch.float32, "lse")
+    st = load().fa_fwd_bf16_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), ls.data_ptr(), B, Hq,
+                                   Hkv, Nq, Nk, d, int(bool(causal)), scale, splits, ws_ptr, ws_bytes, _stream(q))
+    _check("fa_fwd_bf16_decode", st)
     return o, ls
 
 

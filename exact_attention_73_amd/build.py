@@ -12,7 +12,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["fa_api.cpp", "fa_fwd_bf16.hip", "fa_bwd_bf16.hip", "fa_fp8.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd_bf16.hip", "fa_decode_bf16.hip", "fa_bwd_bf16.hip", "fa_fp8.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -52,6 +52,25 @@ int check_shape(int B, int H, int N, int d) {
 
 int check_scale(float s) { return (std::isfinite(s) && s > 0.f) ? FA_OK : FA_ERR_ARG; }
 
+// sizes of the decode entry points (grouped KV heads, unequal lengths)
+int check_decode_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+  const bool dok = d == 64 || d == 128 || d == 256;
+  const int dd = dok ? d : 1;
+  if (Hkv < 1 || Nk < 1) return FA_ERR_SHAPE;
+  if (int e = check_shape(B, Hq, Nq, dd)) return e;
+  if (int e = check_shape(B, Hkv, Nk, dd)) return e;
+  if (Hq % Hkv) return FA_ERR_SHAPE;
+  // 32-key tile offsets run up to 31 rows past the last key
+  if ((double)(Nk + 32) * (double)dd * 2.0 >= 2147483648.0) return FA_ERR_SHAPE;
+  if (!dok) return FA_ERR_HEADDIM;
+  return FA_OK;
+}
+
+long long decode_workspace_bytes(int B, int Hq, int Nq, int d, int splits) {
+  if (splits <= 1) return 0;
+  return (long long)splits * B * Hq * Nq * (long long)(d + 1) * 4;
+}
+
 int launch_status(hipError_t e) {
   if (e == hipSuccess) return FA_OK;
   (void)hipGetLastError();
@@ -74,6 +93,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case FA_ERR_DEVICE: return "no HIP device, or the current device is not gfx950";
     case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_WORKSPACE: return "workspace missing or smaller than the split count needs";
     default: return "unknown status";
   }
 }
@@ -134,6 +154,56 @@ int fa_fwd_bf16_gqa(const void* q, const void* k, const void* v, float* o, float
   p.scale = softmax_scale;
   p.c = softmax_scale * 1.4426950408889634f;
   return launch_status(fa::launch_fwd_bf16(p, d, causal == 1, static_cast<hipStream_t>(stream)));
+}
+
+int fa_fwd_bf16_decode_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits, int num_cus) {
+  if (int e = check_decode_shape(B, Hq, Hkv, Nq, Nk, d)) return e;
+  if (num_splits < 0 || num_cus < 0 || (num_splits == 0 && num_cus < 1)) return FA_ERR_ARG;
+  return fa::dec_bf16_splits(B, Hq, Hkv, Nq, Nk, d, num_splits, num_cus);
+}
+
+long long fa_fwd_bf16_decode_workspace(int B, int Hq, int Nq, int d, int splits) {
+  if (B < 1 || Hq < 1 || Nq < 1 || splits < 1 || (d != 64 && d != 128 && d != 256)) return FA_ERR_ARG;
+  return decode_workspace_bytes(B, Hq, Nq, d, splits);
+}
+
+int fa_fwd_bf16_decode(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Hq, int Hkv,
+                       int Nq, int Nk, int d, int causal, float softmax_scale, int num_splits, void* workspace,
+                       long long workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_PTR;
+  if (int e = check_decode_shape(B, Hq, Hkv, Nq, Nk, d)) return e;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (int e = check_scale(softmax_scale)) return e;
+  if (num_splits < 1) return FA_ERR_ARG;
+  const int splits = fa::dec_bf16_splits(B, Hq, Hkv, Nq, Nk, d, num_splits, 0);
+  const double units = (double)B * Hkv * (((double)(Hq / Hkv) * Nq + 31) / 32);
+  if (units * splits >= 2147483647.0) return FA_ERR_SHAPE;
+  const long long need = decode_workspace_bytes(B, Hq, Nq, d, splits);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  if (need > 0 && !aligned16(workspace)) return FA_ERR_ALIGN;
+  if (int e = check_device()) return e;
+
+  fa::DecBf16Params p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = o;
+  p.lse = lse;
+  const size_t rows = (size_t)B * Hq * Nq;
+  p.part_o = need > 0 ? static_cast<float*>(workspace) : nullptr;
+  p.part_lse = need > 0 ? static_cast<float*>(workspace) + (size_t)splits * rows * d : nullptr;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.splits = splits;
+  const int ntile = (Nk + 31) / 32;
+  p.chunk_tiles = (ntile + splits - 1) / splits;
+  p.scale = softmax_scale;
+  p.c = softmax_scale * 1.4426950408889634f;
+  return launch_status(fa::launch_dec_bf16(p, d, causal == 1, static_cast<hipStream_t>(stream)));
 }
 
 int fa_bwd_bf16(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,

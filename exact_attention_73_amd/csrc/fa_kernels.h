@@ -22,6 +22,26 @@ struct FwdBf16Params {
 
 hipError_t launch_fwd_bf16(const FwdBf16Params& p, int d, bool causal, hipStream_t stream);
 
+struct DecBf16Params {
+  const uint16_t* q;  // bf16 [B, Hq, Nq, d]
+  const uint16_t* k;  // bf16 [B, Hkv, Nk, d]
+  const uint16_t* v;
+  float* o;           // fp32 [B, Hq, Nq, d]
+  float* lse;         // fp32 [B, Hq, Nq]
+  float* part_o;      // fp32 [splits, B * Hq * Nq, d] chunk results (splits > 1)
+  float* part_lse;    // fp32 [splits, B * Hq * Nq]
+  int B, Hq, Hkv, Nq, Nk;
+  int splits;       // key chunks per KV head (non-empty)
+  int chunk_tiles;  // 32-key tiles per chunk
+  float scale;      // softmax scale
+  float c;          // scale * log2(e)
+};
+
+hipError_t launch_dec_bf16(const DecBf16Params& p, int d, bool causal, hipStream_t stream);
+// Key chunks per KV head: `requested` >= 1 reduced to the non-empty count,
+// or 0 for the cost model's choice on a device with num_cus compute units.
+int dec_bf16_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int requested, int num_cus);
+
 struct BwdBf16Params {
   const uint16_t* q;     // bf16 [B, H, N, d]
   const uint16_t* k;

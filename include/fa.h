@@ -51,7 +51,8 @@ enum fa_status {
   FA_ERR_ARG = -4,      /* causal not 0/1, scale not finite and > 0, bad flags     */
   FA_ERR_ALIGN = -5,    /* a pointer is not 16-byte aligned                        */
   FA_ERR_DEVICE = -6,   /* no device, or the current device is not gfx950          */
-  FA_ERR_LAUNCH = -7    /* the kernel launch itself failed                         */
+  FA_ERR_LAUNCH = -7,   /* the kernel launch itself failed                         */
+  FA_ERR_WORKSPACE = -8 /* workspace missing or smaller than the split count needs */
 };
 
 /* Flags of fa_fp8_prep. */
@@ -93,6 +94,55 @@ int fa_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* ls
  */
 int fa_fwd_bf16_gqa(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Hq, int Hkv,
                     int Nq, int Nk, int d, int causal, float softmax_scale, void* stream);
+
+/*
+ * Decode-shaped forward: a few queries per head against a long key/value
+ * sequence.  The FA3 explainer (sections "GQA/MQA 为何改变 Kernel 任务数量"
+ * and "Prefill、Decode 和训练的收益不同") names split-KV and packing the
+ * query heads of a KV head as what gives such shapes enough parallel work.
+ * The result is that of fa_fwd_bf16_gqa (same arguments, same bottom-right
+ * causal reading, O = 0 and lse = -inf for a query that sees no key); only
+ * the work split differs:
+ *
+ *  - The G = Hq / Hkv query heads of a KV head, times Nq queries, are packed
+ *    into 32-row blocks, so one read of a K/V tile serves up to 32 rows.
+ *  - The keys of each KV head are cut into `splits` chunks of whole 32-key
+ *    tiles, one workgroup per (batch, KV head, chunk, row block).  When more
+ *    than one chunk is used, each chunk's normalised O_c and lse_c go to the
+ *    workspace, and a second kernel on the same stream merges them by
+ *    lse = ln sum_c exp(lse_c), O = sum_c exp(lse_c - lse) O_c.
+ *
+ * fa_fwd_bf16_decode_splits -- the chunk count the forward will use.
+ *   num_splits >= 1: that many, reduced to the number of non-empty chunks
+ *   (every chunk holds ceil(tiles / num_splits) tiles).  num_splits = 0: a
+ *   cost model's choice for a device with num_cus compute units (HBM time
+ *   of the K/V stream in rounds of resident workgroups, plus the partial
+ *   results' traffic and one more launch when there is more than one chunk).
+ *   Host only, no device needed.  Returns >= 1, or FA_ERR_SHAPE /
+ *   FA_ERR_HEADDIM as fa_fwd_bf16_decode would, or FA_ERR_ARG for a
+ *   negative count or num_splits = 0 without num_cus.
+ *
+ * fa_fwd_bf16_decode_workspace -- bytes of workspace for `splits` chunks:
+ *   0 when splits = 1, else splits * B * Hq * Nq * (d + 1) * 4.
+ *   FA_ERR_ARG for sizes < 1 or an unsupported d.
+ *
+ * fa_fwd_bf16_decode -- the forward.
+ *   q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, softmax_scale: as
+ *   fa_fwd_bf16_gqa (also FA_ERR_SHAPE when (Nk + 32) * d * 2 >= 2^31).
+ *   num_splits : >= 1, reduced as fa_fwd_bf16_decode_splits does
+ *                (FA_ERR_ARG for < 1).
+ *   workspace  : device memory, 16-byte aligned, owned by the caller, at
+ *                least fa_fwd_bf16_decode_workspace(effective splits) bytes
+ *                (FA_ERR_WORKSPACE otherwise); unused, and may be NULL,
+ *                when the effective count is 1.  Its contents on entry do
+ *                not matter, and on return they are scratch.  Calls that
+ *                share a workspace must not overlap in time.
+ */
+int fa_fwd_bf16_decode_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits, int num_cus);
+long long fa_fwd_bf16_decode_workspace(int B, int Hq, int Nq, int d, int splits);
+int fa_fwd_bf16_decode(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Hq, int Hkv,
+                       int Nq, int Nk, int d, int causal, float softmax_scale, int num_splits, void* workspace,
+                       long long workspace_bytes, void* stream);
 
 /*
  * fa_bwd_bf16 -- exact attention backward: dQ, dK, dV of the forward above

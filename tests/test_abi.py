@@ -18,7 +18,7 @@ FAKE = 0x10000  # aligned, never dereferenced (validation fails first)
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(fa_\w+)\s*\(", src, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:long\s+)?\w+\**\s+\**(fa_\w+)\s*\(", src, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -80,6 +80,34 @@ def test_gqa_validation(lib):
     assert f(q=None) == -1
     assert f(Hkv=0) == -2 and f(Nk=0) == -2 and f(Hq=6, Hkv=4) == -2 and f(Nq=0) == -2
     assert f(d=96) == -3 and f(causal=2) == -4
+
+
+def test_decode_splits_and_workspace(lib):
+    sp = lambda B=1, Hq=32, Hkv=8, Nq=1, Nk=131072, d=128, n=0, cus=256: lib.fa_fwd_bf16_decode_splits(
+        B, Hq, Hkv, Nq, Nk, d, n, cus)
+    # a request is reduced to the number of non-empty chunks of 32-key tiles
+    assert sp(Nk=100, n=7) == 4 and sp(Nk=128, n=3) == 2 and sp(Nk=1000, n=1) == 1 and sp(Nk=5, n=9) == 1
+    # the cost model: 8 KV heads on 256 CUs take 32 chunks each (one workgroup per CU);
+    # 64 sequences x 8 KV heads already fill the device with one chunk
+    assert sp() == 32 and sp(B=64, Nk=8192) == 1
+    assert sp(Nk=64) == 1  # too few tiles to share between the waves of two chunks
+    assert sp(Hq=6, Hkv=4) == -2 and sp(d=96) == -3 and sp(n=-1) == -4 and sp(cus=0) == -4
+    ws = lib.fa_fwd_bf16_decode_workspace
+    assert ws(1, 32, 1, 128, 1) == 0 and ws(2, 4, 3, 64, 5) == 5 * 2 * 4 * 3 * 65 * 4
+    assert ws(0, 1, 1, 128, 2) == -4 and ws(1, 1, 1, 96, 2) == -4 and ws(1, 1, 1, 128, 0) == -4
+
+
+def test_decode_validation(lib):
+    f = lambda **kw: lib.fa_fwd_bf16_decode(kw.get("q", FAKE), FAKE, FAKE, FAKE, FAKE, 1, kw.get("Hq", 8),
+                                            kw.get("Hkv", 2), 1, kw.get("Nk", 4096), kw.get("d", 128),
+                                            kw.get("causal", 0), 0.1, kw.get("splits", 4), kw.get("ws", FAKE),
+                                            kw.get("wsb", 1 << 20), None)
+    assert f(q=None) == -1
+    assert f(Hkv=3) == -2 and f(Nk=0) == -2 and f(Nk=1 << 23) == -2  # (Nk + 32) * d * 2 >= 2^31
+    assert f(d=32) == -3 and f(causal=2) == -4 and f(splits=0) == -4
+    need = 4 * 8 * 129 * 4
+    assert f(ws=None) == -8 and f(wsb=need - 1) == -8 and f(ws=FAKE + 4, wsb=need) == -5
+    assert f(ws=None, splits=1) != -8  # one chunk needs no workspace
 
 
 def test_bwd_validation(lib):
