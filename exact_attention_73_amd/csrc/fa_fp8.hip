@@ -44,8 +44,13 @@ constexpr float kE4M3Max = 448.f;
 // ---------------------------------------------------------------------------
 enum PrepMode { kPrepFused = 0, kPrepAmaxOnly = 1, kPrepGlobalScale = 2 };
 
+// Four floats to E4M3 (round to nearest even), packed low to high.  The
+// first conversion writes bytes 0-1 and keeps the upper half of its `old`
+// operand, which the second conversion then overwrites, so `old` may be
+// any value: a's own bits, whose register is free after this conversion,
+// spare a zero initialisation.
 __device__ __forceinline__ uint32_t cvt_e4m3x4(float a, float b, float c, float d) {
-  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_uint(a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 

@@ -125,7 +125,7 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* src) {
 #define FA_VLEAD 4
 #endif
 #ifndef FA_VPM
-#define FA_VPM 5
+#define FA_VPM 3
 #endif
 #ifndef FA_VPP
 #define FA_VPP 2
