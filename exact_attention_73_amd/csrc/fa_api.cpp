@@ -37,6 +37,25 @@ int check_device() {
   return st == 1 ? FA_OK : FA_ERR_DEVICE;
 }
 
+// Compute units of the current device (cached per device; 0 if unknown).
+std::atomic<int> g_cus[kMaxDevices];
+int device_cus() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  int n = g_cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    g_cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_shape(int B, int H, int N, int d) {
@@ -237,6 +256,11 @@ int fa_bwd_bf16(const void* q, const void* k, const void* v, const float* o, con
   p.N = N;
   p.scale = softmax_scale;
   p.c = softmax_scale * 1.4426950408889634f;
+  // two dK/dV launches pay off once the grid (one workgroup per 128 keys of
+  // a head) fills every CU; below that the single launch is faster
+  const double wgs = (double)B * H * ((N + 127) / 128);
+  const int cus = device_cus();
+  p.split_dkdv = (d == 128 && cus > 0 && wgs >= cus) ? 1 : 0;
   return launch_status(fa::launch_bwd_bf16(p, d, causal == 1, static_cast<hipStream_t>(stream)));
 }
 

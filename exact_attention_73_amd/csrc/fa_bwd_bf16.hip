@@ -22,6 +22,14 @@
 //    P, dS leave the accumulators as the B operands of dV^T += dO^T P and
 //    dK^T += Q^T dS, whose A operands come from transposed LDS reads of the
 //    same tiles in the matching query order (the forward's PV trick).
+//    At d = 128 a wave holding both accumulators needs more than 256
+//    registers (one wave per SIMD).  When the grid has at least one
+//    workgroup per CU the kernel runs as two launches instead, one
+//    accumulating dV only (S and dV^T products) and one dK only (S, dP and
+//    dK^T products, 32-query tiles): each fits 256 registers, so two waves
+//    share every SIMD, which outweighs computing S twice.  The arithmetic
+//    and its order are those of the single kernel, so results are the same
+//    bit for bit.
 //  * bwd_dq_kernel: shaped like the forward: one workgroup per 128 queries,
 //    Q and dO resident as B operands, K and V tiles of 64 keys through the
 //    LDS ring; S^T = K Q^T, dP^T = V dO^T (a lane owns one query, so lse and
@@ -132,14 +140,20 @@ constexpr int kBwdThreads = kBwdWaves * 64;
 // K, V rows and the dK, dV accumulators of a dK/dV wave need more than 256
 // registers; the dQ kernel fits 256 at both head sizes (measured: two per
 // CU is 18 % faster than one at d = 128).
+// PART of the dK/dV work a launch does: both gradients, dV only, dK only.
+enum DkdvPart { kBoth = 0, kDvOnly = 1, kDkOnly = 2 };
+
 template <int D> struct BwdCfg {
-  static constexpr int kDkdvMinb = D == 64 ? 2 : 1;
+  static constexpr int kDkdvMinb = D == 64 ? 2 : 1;  // both gradients in one wave
   static constexpr int kDqMinb = 2;
 };
+template <int D, int PART> constexpr int dkdv_minb() { return PART == kBoth ? BwdCfg<D>::kDkdvMinb : 2; }
+template <int PART> constexpr int dkdv_bq() { return PART == kDkOnly ? 32 : 64; }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, BwdCfg<D>::kDkdvMinb) void bwd_dkdv_kernel(BwdBf16Params p) {
-  constexpr int BQ = 64;             // queries per tile
+template <int D, bool CAUSAL, int PART>
+__global__ __launch_bounds__(kBwdThreads, (dkdv_minb<D, PART>())) void bwd_dkdv_kernel(BwdBf16Params p) {
+  constexpr bool DO_V = PART != kDkOnly, DO_K = PART != kDvOnly;
+  constexpr int BQ = dkdv_bq<PART>();  // queries per tile
   constexpr int NQB = BQ / 32;       // 32-query blocks per tile
   constexpr int NQS = D / 16;        // k-steps over d
   constexpr int NDB = D / 32;        // 32-row blocks of dK^T, dV^T
@@ -236,7 +250,7 @@ __global__ __launch_bounds__(kBwdThreads, BwdCfg<D>::kDkdvMinb) void bwd_dkdv_ke
 #pragma unroll
       for (int st = 0; st < NQS; ++st) {
         s = mfma_bf16_32x32x16(read_row<D>(qs, row, st, hi), kb[st], s);
-        dp = mfma_bf16_32x32x16(read_row<D>(gs, row, st, hi), vb[st], dp);
+        if constexpr (DO_K) dp = mfma_bf16_32x32x16(read_row<D>(gs, row, st, hi), vb[st], dp);
       }
       // register r holds query qb*32 + 8 (r / 4) + 4 hi + (r % 4)
 #pragma unroll
@@ -252,18 +266,28 @@ __global__ __launch_bounds__(kBwdThreads, BwdCfg<D>::kDkdvMinb) void bwd_dkdv_ke
             pv = key > q ? 0.f : pv;
           }
           s[r] = pv;
-          dp[r] = pv * (dp[r] - dd[e]);
+          if constexpr (DO_K) dp[r] = pv * (dp[r] - dd[e]);
         }
       }
       // dV^T += dO^T P and dK^T += Q^T dS over this block's 32 queries
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 pb = pack8(s, ks), sb = pack8(dp, ks);
         const int rbase = qb * 32 + 16 * ks;
+        if constexpr (DO_V && DO_K) {
+          const bf16x8 pb = pack8(s, ks), sb = pack8(dp, ks);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          dv[db] = mfma_bf16_32x32x16(read_cols<D>(gs, rbase, 32 * db, lane), pb, dv[db]);
-          dk[db] = mfma_bf16_32x32x16(read_cols<D>(qs, rbase, 32 * db, lane), sb, dk[db]);
+          for (int db = 0; db < NDB; ++db) {
+            dv[db] = mfma_bf16_32x32x16(read_cols<D>(gs, rbase, 32 * db, lane), pb, dv[db]);
+            dk[db] = mfma_bf16_32x32x16(read_cols<D>(qs, rbase, 32 * db, lane), sb, dk[db]);
+          }
+        } else if constexpr (DO_V) {
+          const bf16x8 pb = pack8(s, ks);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) dv[db] = mfma_bf16_32x32x16(read_cols<D>(gs, rbase, 32 * db, lane), pb, dv[db]);
+        } else {
+          const bf16x8 sb = pack8(dp, ks);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) dk[db] = mfma_bf16_32x32x16(read_cols<D>(qs, rbase, 32 * db, lane), sb, dk[db]);
         }
       }
     }
@@ -288,8 +312,8 @@ __global__ __launch_bounds__(kBwdThreads, BwdCfg<D>::kDkdvMinb) void bwd_dkdv_ke
         const f32x4 a = {dk[db][4 * g] * p.scale, dk[db][4 * g + 1] * p.scale, dk[db][4 * g + 2] * p.scale,
                          dk[db][4 * g + 3] * p.scale};
         const f32x4 b = {dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
-        *reinterpret_cast<f32x4*>(dkr + db * 32 + 8 * g + 4 * hi) = a;
-        *reinterpret_cast<f32x4*>(dvr + db * 32 + 8 * g + 4 * hi) = b;
+        if constexpr (DO_K) *reinterpret_cast<f32x4*>(dkr + db * 32 + 8 * g + 4 * hi) = a;
+        if constexpr (DO_V) *reinterpret_cast<f32x4*>(dvr + db * 32 + 8 * g + 4 * hi) = b;
       }
   }
 }
@@ -435,7 +459,15 @@ hipError_t launch(const BwdBf16Params& p, hipStream_t stream) {
                      p.delta, rows);
   const unsigned bh = (unsigned)p.B * (unsigned)p.H;
   const unsigned tiles = (unsigned)((p.N + 127) / 128);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(bh * tiles), dim3(kBwdThreads), 0, stream, p);
+  bool split = false;
+  if constexpr (D == 128) {
+    if (p.split_dkdv) {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kDvOnly>), dim3(bh * tiles), dim3(kBwdThreads), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kDkOnly>), dim3(bh * tiles), dim3(kBwdThreads), 0, stream, p);
+      split = true;
+    }
+  }
+  if (!split) hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kBoth>), dim3(bh * tiles), dim3(kBwdThreads), 0, stream, p);
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(bh * tiles), dim3(kBwdThreads), 0, stream, p);
   return hipGetLastError();
 }

@@ -56,6 +56,7 @@ struct BwdBf16Params {
   int B, H, N;
   float scale;  // softmax scale
   float c;      // scale * log2(e)
+  int split_dkdv;  // d = 128: dV and dK in two launches (set when the grid fills the device)
 };
 
 hipError_t launch_bwd_bf16(const BwdBf16Params& p, int d, bool causal, hipStream_t stream);

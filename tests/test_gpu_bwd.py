@@ -69,6 +69,26 @@ def test_bwd_std_block_sampled_heads(causal):
         _check((dq[sl], dk[sl], dv[sl]), ref, f"std b={b} h={h} causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_split_launches_match_single_launch(causal):
+    # B4 H16 N1000 d128 fills the device (512 workgroups of 128 keys), so dK
+    # and dV come from two launches; head 0 alone (8 workgroups) takes the
+    # single dK/dV launch.  Same arithmetic in the same order: equal bit for bit.
+    q, k, v = (x.cuda() for x in make_qkv(4, 16, 1000, 128, seed=6300))
+    do = make_do(4, 16, 1000, 128, seed=6300).cuda()
+    o, lse = fa.fwd_bf16(q, k, v, causal=causal)
+    big = fa.bwd_bf16(q, k, v, o, lse, do, causal=causal)
+    one = [x[:1, :1].contiguous() for x in (q, k, v, o, lse, do)]
+    small = fa.bwd_bf16(*one, causal=causal)
+    torch.cuda.synchronize()
+    for g_big, g_small in zip(big, small):
+        assert torch.equal(g_big[:1, :1], g_small)
+    # and the tiled tail against the oracle on a sampled head
+    ref = attention_bwd_ref(q[1:2, 5:6].cpu(), k[1:2, 5:6].cpu(), v[1:2, 5:6].cpu(), do[1:2, 5:6].cpu(), causal=causal,
+                            scale=softmax_scale(128))
+    _check(tuple(g[1:2, 5:6].cpu().numpy() for g in big), ref, f"split launches causal={causal}")
+
+
 def test_bwd_deterministic():
     q, k, v = make_qkv(1, 4, 777, 128, seed=6200)
     do = make_do(1, 4, 777, 128, seed=6200)
