@@ -1,5 +1,7 @@
 /*
- * fa.h -- C ABI of the MI355X (gfx950) fused exact attention forward library.
+ * fa.h -- C ABI of the MI355X (gfx950) fused exact attention library
+ * (forward in bf16 and FP8, grouped-head and decode-shaped forwards, and
+ * the bf16 backward).
  *
  * The library computes O = softmax(scale * Q K^T) V and the row logsumexp,
  * tile by tile with an online softmax, without ever writing the N x N score
@@ -13,9 +15,10 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - All tensor pointers are DEVICE pointers owned by the caller.  The
- *   library allocates no memory and keeps no state besides a per-device
- *   cache of the device's architecture check; it is safe to call from
- *   several host threads.
+ *   library allocates no memory (entry points that need scratch memory
+ *   take a caller-owned workspace) and keeps no state besides a per-device
+ *   cache of the architecture check and the compute-unit count; it is safe
+ *   to call from several host threads.
  * - Tensors are dense row-major ("contiguous").  Layout [B, H, N, d] means
  *   element (b, h, n, i) sits at ((b * H + h) * N + n) * d + i.
  * - Every pointer must be 16-byte aligned (FA_ERR_ALIGN otherwise).
@@ -29,8 +32,9 @@
  * - There is no fallback: a case the kernels do not cover is an error,
  *   never a slower path.  The kernels are built for gfx950 only; any other
  *   device gives FA_ERR_DEVICE.
- * - Causal masking: query row i attends to key j iff j <= i (queries and
- *   keys have the same length N).
+ * - Causal masking: query row i attends to key j iff j <= i when queries
+ *   and keys have the same length N; the entry points for Nq queries and
+ *   Nk keys align the mask bottom-right, j <= i + Nk - Nq.
  * - logsumexp is the natural log of sum_j exp(scale * q_i . k_j) over the
  *   keys row i attends to, fp32 [B, H, N].
  */
