@@ -23,7 +23,8 @@ Modules:
 * :mod:`oracle.gqa` -- ``attention_gqa_ref`` (grouped/multi-query heads,
   unequal query and key lengths, bottom-right causal alignment).
 * :mod:`oracle.backward` -- ``attention_bwd_ref`` (dQ, dK, dV of the
-  definition, written out).
+  definition, written out) and ``attention_gqa_bwd_ref`` (grouped heads:
+  each KV head's gradient summed over the query heads that read it).
 * :mod:`oracle.fp8` -- OCP E4M3 codec, Sylvester Hadamard rotation, per-block
   and per-tensor scaling, and ``fp8_attention_emulate``.
 
@@ -35,7 +36,7 @@ marked "parity unpinned" in :mod:`oracle.fp8`.
 """
 
 from .attention import attention_ref, online_ref  # noqa: F401
-from .backward import attention_bwd_ref  # noqa: F401
+from .backward import attention_bwd_ref, attention_gqa_bwd_ref  # noqa: F401
 from .gqa import attention_gqa_ref  # noqa: F401
 from .fp8 import (  # noqa: F401
     E4M3_MAX,

@@ -28,7 +28,7 @@ import numpy as np
 
 from .attention import scale_f64, to_f64
 
-__all__ = ["attention_bwd_ref"]
+__all__ = ["attention_bwd_ref", "attention_gqa_bwd_ref"]
 
 
 def attention_bwd_ref(q, k, v, do, causal: bool = False, scale=None, row_block: int = 1024):
@@ -70,4 +70,41 @@ def attention_bwd_ref(q, k, v, do, causal: bool = False, scale=None, row_block: 
                 dq[b, h, r0:r1] = sc * (dS @ K)
                 dk[b, h] += sc * (dS.T @ Q[r0:r1])
                 dv[b, h] += P.T @ dOb
+    return dq, dk, dv
+
+
+def attention_gqa_bwd_ref(q, k, v, do, causal: bool = False, scale=None, row_block: int = 1024):
+    """dQ, dK, dV with grouped/multi-query heads (equal query and key lengths).
+
+    The forward of :mod:`oracle.gqa` lets query head h read KV head
+    floor(h / G), G = Hq / Hkv: the same as giving every query head its own
+    copy of that KV head.  By the chain rule, the gradient of a KV head is
+    then the sum of the gradients of its G copies, each of which is the
+    single-head gradient written out in :func:`attention_bwd_ref`.
+
+    Args:
+      q, do: ``[B, Hq, N, d]``; k, v: ``[B, Hkv, N, d]`` (Hq a multiple of Hkv).
+      causal, scale, row_block: as :func:`attention_bwd_ref`.
+
+    Returns:
+      ``(dq, dk, dv)`` float64 arrays shaped like ``q``, ``k``, ``v``.
+    """
+    q, k, v, do = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if k.shape[2] != N:
+        raise ValueError("queries and keys must have the same length")
+    G = Hq // Hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for h in range(Hq):
+        hk = h // G
+        gq, gk, gv = attention_bwd_ref(q[:, h:h + 1], k[:, hk:hk + 1], v[:, hk:hk + 1], do[:, h:h + 1],
+                                       causal=causal, scale=scale, row_block=row_block)
+        dq[:, h] = gq[:, 0]
+        dk[:, hk] += gk[:, 0]
+        dv[:, hk] += gv[:, 0]
     return dq, dk, dv

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention_bwd_ref, attention_ref
+from oracle import attention_bwd_ref, attention_gqa_bwd_ref, attention_ref
 
 RNG = np.random.default_rng(20)
 
@@ -87,3 +87,47 @@ def test_q_zero_closed_form():
     np.testing.assert_allclose(dq[0, 0], expect, atol=1e-12)
     np.testing.assert_allclose(dk, 0.0, atol=1e-12)
     np.testing.assert_allclose(dv[0, 0], np.repeat(do[0, 0].mean(axis=0, keepdims=True), N, axis=0), atol=1e-12)
+
+
+def _autograd_gqa(q, k, v, do, causal, scale):
+    # the grouped forward with every query head given its own copy of its KV
+    # head (repeat_interleave); autograd sums the gradient over the copies
+    t = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v)]
+    G = q.shape[1] // k.shape[1]
+    kk, vv = t[1].repeat_interleave(G, dim=1), t[2].repeat_interleave(G, dim=1)
+    s = scale * t[0] @ kk.transpose(-1, -2)
+    if causal:
+        n = q.shape[2]
+        s = s.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), float("-inf"))
+    o = torch.softmax(s, dim=-1) @ vv
+    o.backward(torch.tensor(do))
+    return [x.grad.numpy() for x in t]
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (6, 1), (8, 4)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_matches_float64_autograd(Hq, Hkv, causal):
+    B, N, d = 2, 45, 16
+    q, do = (RNG.standard_normal((B, Hq, N, d)) for _ in range(2))
+    k, v = (RNG.standard_normal((B, Hkv, N, d)) for _ in range(2))
+    got = attention_gqa_bwd_ref(q, k, v, do, causal=causal, scale=0.3, row_block=16)
+    ref = _autograd_gqa(q, k, v, do, causal, float(np.float32(0.3)))
+    for g, r in zip(got, ref):
+        np.testing.assert_allclose(g, r, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_one_group_is_the_square_backward(causal):
+    q, k, v, do = (RNG.standard_normal((1, 3, 30, 8)) for _ in range(4))
+    for g, r in zip(attention_gqa_bwd_ref(q, k, v, do, causal=causal), attention_bwd_ref(q, k, v, do, causal=causal)):
+        np.testing.assert_allclose(g, r, atol=1e-13)
+
+
+def test_gqa_dv_column_sum():
+    # rows of P sum to 1, so summed over keys, a KV head's dV is the sum of dO
+    # over all query rows of all G query heads that read it
+    q, do = (RNG.standard_normal((1, 6, 20, 8)) for _ in range(2))
+    k, v = (RNG.standard_normal((1, 2, 20, 8)) for _ in range(2))
+    _, _, dv = attention_gqa_bwd_ref(q, k, v, do, causal=True)
+    for hk in range(2):
+        np.testing.assert_allclose(dv[0, hk].sum(axis=0), do[0, 3 * hk:3 * hk + 3].sum(axis=(0, 1)), atol=1e-12)
