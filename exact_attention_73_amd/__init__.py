@@ -8,6 +8,7 @@ here only marshal torch tensors into that ABI.
 from ._lib import (  # noqa: F401
     FaError,
     bwd_bf16,
+    bwd_bf16_gqa,
     decode_splits,
     decode_workspace_bytes,
     fp8_prep,
@@ -21,4 +22,4 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["fwd_bf16", "fwd_bf16_gqa", "fwd_bf16_decode", "decode_splits", "decode_workspace_bytes",
-           "bwd_bf16", "fp8_prep", "fp8_prep_v", "fwd_fp8", "fp8_vt_ld", "load", "FaError"]
+           "bwd_bf16", "bwd_bf16_gqa", "fp8_prep", "fp8_prep_v", "fwd_fp8", "fp8_vt_ld", "load", "FaError"]

@@ -29,6 +29,7 @@ SIGNATURES = {
     "fa_fwd_bf16_decode_splits": (_I, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "fa_fwd_bf16_decode_workspace": (_LL, [_I, _I, _I, _I, _I]),
     "fa_fwd_bf16_decode": (_I, [_VP, _VP, _VP, _FP, _FP, _I, _I, _I, _I, _I, _I, _I, _F, _I, _VP, _LL, _VP]),
+    "fa_bwd_bf16_gqa": (_I, [_VP, _VP, _VP, _FP, _FP, _VP, _FP, _FP, _FP, _FP, _I, _I, _I, _I, _I, _I, _F, _VP]),
     "fa_bwd_bf16": (_I, [_VP, _VP, _VP, _FP, _FP, _VP, _FP, _FP, _FP, _FP, _I, _I, _I, _I, _I, _F, _VP]),
     "fa_fp8_prep": (_I, [_VP, _VP, _FP, _VP, _I, _I, _I, _I, ctypes.c_uint, _VP]),
     "fa_fp8_vt_ld": (_I, [_I]),
@@ -176,31 +177,52 @@ def bwd_bf16(q, k, v, o, lse, dout, causal: bool = False, softmax_scale: float |
     """dQ, dK, dV (fp32 ``[B, H, N, d]``) of the forward for the upstream
     gradient ``dout`` (bf16), from the forward's ``o`` and ``lse`` (fp32).
     ``delta`` is the fp32 ``[B, H, N]`` workspace (allocated when omitted)."""
+    return _bwd("fa_bwd_bf16", q, k, v, o, lse, dout, causal, softmax_scale, dq, dk, dv, delta)
+
+
+def bwd_bf16_gqa(q, k, v, o, lse, dout, causal: bool = False, softmax_scale: float | None = None, dq=None, dk=None,
+                 dv=None, delta=None):
+    """Backward with grouped/multi-query heads: q, dout, o ``[B, Hq, N, d]``,
+    k, v ``[B, Hkv, N, d]``; returns fp32 dq ``[B, Hq, N, d]`` and dk, dv
+    ``[B, Hkv, N, d]`` (each KV head's gradient summed over its query heads)."""
+    return _bwd("fa_bwd_bf16_gqa", q, k, v, o, lse, dout, causal, softmax_scale, dq, dk, dv, delta)
+
+
+def _bwd(fn, q, k, v, o, lse, dout, causal, softmax_scale, dq, dk, dv, delta):
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _need(t, torch.bfloat16, n)
     _need(o, torch.float32, "o")
     _need(lse, torch.float32, "lse")
-    if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, dout, o)):
-        raise ValueError("q, k, v, dout, o must share one shape [B, H, N, d]")
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or any(t.shape != q.shape for t in (dout, o)):
+        raise ValueError("q, dout, o must be [B, Hq, N, d] and k, v [B, Hkv, N, d]")
     B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError("k, v must be [B, Hkv, N, d] with the queries' B, N, d")
+    if fn == "fa_bwd_bf16" and Hkv != H:
+        raise ValueError("q, k, v, dout, o must share one shape [B, H, N, d] (use bwd_bf16_gqa for grouped heads)")
     if tuple(lse.shape) != (B, H, N):
         raise ValueError("lse must be [B, H, N]")
     scale = (1.0 / d ** 0.5) if softmax_scale is None else float(softmax_scale)
     outs = []
-    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
-        t = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if t is None else t
+    for t, n, h in ((dq, "dq", H), (dk, "dk", Hkv), (dv, "dv", Hkv)):
+        t = torch.empty((B, h, N, d), dtype=torch.float32, device=q.device) if t is None else t
         _need(t, torch.float32, n)
-        if tuple(t.shape) != (B, H, N, d):
-            raise ValueError(f"{n} must be [B, H, N, d]")
+        if tuple(t.shape) != (B, h, N, d):
+            raise ValueError(f"{n} must be [B, {h}, N, d]")
         outs.append(t)
     ws = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
     _need(ws, torch.float32, "delta")
     if tuple(ws.shape) != (B, H, N):
         raise ValueError("delta must be [B, H, N]")
-    st = load().fa_bwd_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-                            outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(), ws.data_ptr(), B, H, N, d,
-                            int(bool(causal)), scale, _stream(q))
-    _check("fa_bwd_bf16", st)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+            outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(), ws.data_ptr())
+    lib = load()
+    if fn == "fa_bwd_bf16":
+        st = lib.fa_bwd_bf16(*ptrs, B, H, N, d, int(bool(causal)), scale, _stream(q))
+    else:
+        st = lib.fa_bwd_bf16_gqa(*ptrs, B, H, Hkv, N, d, int(bool(causal)), scale, _stream(q))
+    _check(fn, st)
     return tuple(outs)
 
 

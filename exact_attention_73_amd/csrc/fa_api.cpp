@@ -225,11 +225,16 @@ int fa_fwd_bf16_decode(const void* q, const void* k, const void* v, float* o, fl
   return launch_status(fa::launch_dec_bf16(p, d, causal == 1, static_cast<hipStream_t>(stream)));
 }
 
-int fa_bwd_bf16(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
-                float* dq, float* dk, float* dv, float* delta_ws, int B, int H, int N, int d, int causal,
-                float softmax_scale, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int bwd_common(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
+               float* dq, float* dk, float* dv, float* delta_ws, int B, int H, int Hkv, int N, int d, int causal,
+               float softmax_scale, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta_ws) return FA_ERR_NULL_PTR;
   if (int e = check_shape(B, H, N, d == 64 || d == 128 ? d : 1)) return e;
+  if (Hkv < 1 || H % Hkv) return FA_ERR_SHAPE;
   // fp32 [N, d] slices are addressed with 32-bit byte offsets too
   if ((double)N * (double)d * 4.0 >= 2147483648.0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
@@ -254,14 +259,31 @@ int fa_bwd_bf16(const void* q, const void* k, const void* v, const float* o, con
   p.B = B;
   p.H = H;
   p.N = N;
+  p.Hkv = Hkv;
   p.scale = softmax_scale;
   p.c = softmax_scale * 1.4426950408889634f;
-  // two dK/dV launches pay off once the grid (one workgroup per 128 keys of
-  // a head) fills every CU; below that the single launch is faster
-  const double wgs = (double)B * H * ((N + 127) / 128);
+  // two dK/dV launches pay off once their grid (one workgroup per 128 keys
+  // of a KV head) fills every CU; below that the single launch is faster
+  const double wgs = (double)B * Hkv * ((N + 127) / 128);
   const int cus = device_cus();
   p.split_dkdv = (d == 128 && cus > 0 && wgs >= cus) ? 1 : 0;
   return launch_status(fa::launch_bwd_bf16(p, d, causal == 1, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd_bf16(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
+                float* dq, float* dk, float* dv, float* delta_ws, int B, int H, int N, int d, int causal,
+                float softmax_scale, void* stream) {
+  return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, H, H, N, d, causal, softmax_scale, stream);
+}
+
+int fa_bwd_bf16_gqa(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
+                    float* dq, float* dk, float* dv, float* delta_ws, int B, int Hq, int Hkv, int N, int d,
+                    int causal, float softmax_scale, void* stream) {
+  return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, causal, softmax_scale, stream);
 }
 
 int fa_fp8_prep(const void* x, void* x8, float* x_scale, const signed char* signs, int B, int H, int N, int d,

@@ -14,7 +14,12 @@
 //
 // Three kernels, no atomics:
 //  * bwd_delta_kernel: D = rowsum(dO * O), one 16-lane group per row.
-//  * bwd_dkdv_kernel: one workgroup per (batch, head, 128 keys); each wave
+// Grouped heads (Hq = G Hkv query heads over Hkv KV heads, equal query and
+// key lengths): a KV head's dK, dV are sums over the G query heads that read
+// it, so a dK/dV workgroup streams the query tiles of all G heads through
+// its ring into the same accumulators; dQ reads its query head's KV head.
+//
+//  * bwd_dkdv_kernel: one workgroup per (batch, KV head, 128 keys); each wave
 //    owns 32 keys and keeps its K and V rows in VGPRs as B operands.  Query
 //    tiles of 64 rows (Q, dO, lse, D) stream through a 2-slot LDS ring
 //    filled by direct-to-LDS loads one tile ahead.  S = Q K^T and dP = dO V^T
@@ -169,21 +174,24 @@ __global__ __launch_bounds__(kBwdThreads, (dkdv_minb<D, PART>())) void bwd_dkdv_
   __shared__ __attribute__((aligned(16))) float Ls0[BQ], Ls1[BQ], Ds0[BQ], Ds1[BQ];
 
   const int N = p.N;
-  const int BH = p.B * p.H;
+  const int BK = p.B * p.Hkv;       // (batch, KV head) pairs
+  const int G = p.H / p.Hkv;        // query heads per KV head
   const int nk = (N + 127) / 128;
-  int bh, kt;
+  int bk, kt;
   if constexpr (CAUSAL) {
     // the first key tiles see the most query tiles: launch them first
-    kt = (int)blockIdx.x / BH;
-    bh = (int)blockIdx.x % BH;
+    kt = (int)blockIdx.x / BK;
+    bk = (int)blockIdx.x % BK;
   } else {
     const int w = xcd_contiguous((int)blockIdx.x, (int)gridDim.x);
-    bh = w / nk;
+    bk = w / nk;
     kt = w % nk;
   }
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const size_t base = (size_t)bh * N * D;
+  const size_t base = (size_t)bk * N * D;  // k, v, dk, dv
+  // query heads bk * G .. bk * G + G - 1 (b * Hq + h, adjacent) read this KV head
+  const size_t qbh0 = (size_t)bk * G;
   const int kw0 = kt * 128 + wave * 32;  // first key of this wave
   const int key = kw0 + l32;             // the key column this lane owns
 
@@ -202,19 +210,24 @@ __global__ __launch_bounds__(kBwdThreads, (dkdv_minb<D, PART>())) void bwd_dkdv_
 
   const int nq = (N + BQ - 1) / BQ;
   const int j0 = CAUSAL ? (kt * 128) / BQ : 0;  // earlier query tiles see none of these keys
+  const int nqh = nq - j0;                      // query tiles per query head
+  const int ntl = G * nqh;                      // tiles streamed: every query head of the group
 
-  // direct-to-LDS tile loads (rows past N read as zero)
-  const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(p.q + base, N * D * 2);
-  const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(p.dout + base, N * D * 2);
-  const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(p.lse + (size_t)bh * N, N * 4);
-  const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(p.delta + (size_t)bh * N, N * 4);
+  // direct-to-LDS tile loads of tile t = (query head g, query tile j), each
+  // through a buffer range of that head's N rows (rows past N read as zero)
   int off[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
     const int row = (wave * IPW + i) * RPI + lane / CPR, pc = lane % CPR;
     off[i] = row * D * 2 + ((pc ^ swz<D>(row)) * 16);
   }
-  auto issue = [&](uint16_t* qs, uint16_t* gs, float* ls, float* ds, int j) __attribute__((always_inline)) {
+  auto issue = [&](uint16_t* qs, uint16_t* gs, float* ls, float* ds, int t) __attribute__((always_inline)) {
+    const int g = t / nqh, j = j0 + t - g * nqh;
+    const size_t hb = qbh0 + (size_t)g;
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(p.q + hb * N * D, N * D * 2);
+    const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(p.dout + hb * N * D, N * D * 2);
+    const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(p.lse + hb * N, N * 4);
+    const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(p.delta + hb * N, N * 4);
     const int tb = j * BQ * D * 2;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
@@ -234,12 +247,12 @@ __global__ __launch_bounds__(kBwdThreads, (dkdv_minb<D, PART>())) void bwd_dkdv_
   }
   const float c = p.c;
 
-  auto step = [&](int j, const uint16_t* qs, const uint16_t* gs, const float* ls, const float* ds, uint16_t* qn,
+  auto step = [&](int t, const uint16_t* qs, const uint16_t* gs, const float* ls, const float* ds, uint16_t* qn,
                   uint16_t* gn, float* ln, float* dn) __attribute__((always_inline)) {
     wait_vmem_all();
-    __syncthreads();  // tile j is in LDS; every wave is done with tile j - 1
-    if (j + 1 < nq) issue(qn, gn, ln, dn, j + 1);
-    const int q0 = j * BQ;
+    __syncthreads();  // tile t is in LDS; every wave is done with tile t - 1
+    if (t + 1 < ntl) issue(qn, gn, ln, dn, t + 1);
+    const int q0 = (j0 + t % nqh) * BQ;
     if (CAUSAL && q0 + BQ - 1 < kw0) return;  // every query of the tile precedes this wave's keys
     const bool need_mask = CAUSAL && q0 < kw0 + 31;
 
@@ -293,11 +306,11 @@ __global__ __launch_bounds__(kBwdThreads, (dkdv_minb<D, PART>())) void bwd_dkdv_
     }
   };
 
-  if (j0 < nq) {
-    issue(Qs0, Gs0, Ls0, Ds0, j0);
-    for (int j = j0; j < nq; j += 2) {
-      step(j, Qs0, Gs0, Ls0, Ds0, Qs1, Gs1, Ls1, Ds1);
-      if (j + 1 < nq) step(j + 1, Qs1, Gs1, Ls1, Ds1, Qs0, Gs0, Ls0, Ds0);
+  if (ntl > 0) {
+    issue(Qs0, Gs0, Ls0, Ds0, 0);
+    for (int t = 0; t < ntl; t += 2) {
+      step(t, Qs0, Gs0, Ls0, Ds0, Qs1, Gs1, Ls1, Ds1);
+      if (t + 1 < ntl) step(t + 1, Qs1, Gs1, Ls1, Ds1, Qs0, Gs0, Ls0, Ds0);
     }
   }
 
@@ -372,8 +385,11 @@ __global__ __launch_bounds__(kBwdThreads, BwdCfg<D>::kDqMinb) void bwd_dq_kernel
   const int kend = CAUSAL ? min(N, qt * 128 + 128) : N;
   const int ntiles = (kend + BC - 1) / BC;
 
-  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(p.k + base, N * D * 2);
-  const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(p.v + base, N * D * 2);
+  // KV head of this query head: each KV head serves H / Hkv consecutive query heads
+  const int bb = bh / p.H, hh = bh - bb * p.H;
+  const size_t kvbase = ((size_t)bb * p.Hkv + hh / (p.H / p.Hkv)) * N * D;
+  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(p.k + kvbase, N * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(p.v + kvbase, N * D * 2);
   int off[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
@@ -457,17 +473,18 @@ hipError_t launch(const BwdBf16Params& p, hipStream_t stream) {
   const long rows = (long)p.B * p.H * p.N;
   hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p.dout, p.o,
                      p.delta, rows);
-  const unsigned bh = (unsigned)p.B * (unsigned)p.H;
+  const unsigned bh = (unsigned)p.B * (unsigned)p.H;    // dQ: one workgroup per query head's 128 rows
+  const unsigned bk = (unsigned)p.B * (unsigned)p.Hkv;  // dK/dV: one per KV head's 128 keys
   const unsigned tiles = (unsigned)((p.N + 127) / 128);
   bool split = false;
   if constexpr (D == 128) {
     if (p.split_dkdv) {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kDvOnly>), dim3(bh * tiles), dim3(kBwdThreads), 0, stream, p);
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kDkOnly>), dim3(bh * tiles), dim3(kBwdThreads), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kDvOnly>), dim3(bk * tiles), dim3(kBwdThreads), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kDkOnly>), dim3(bk * tiles), dim3(kBwdThreads), 0, stream, p);
       split = true;
     }
   }
-  if (!split) hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kBoth>), dim3(bh * tiles), dim3(kBwdThreads), 0, stream, p);
+  if (!split) hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kBoth>), dim3(bk * tiles), dim3(kBwdThreads), 0, stream, p);
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(bh * tiles), dim3(kBwdThreads), 0, stream, p);
   return hipGetLastError();
 }

@@ -44,16 +44,17 @@ int dec_bf16_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int requested
 
 struct BwdBf16Params {
   const uint16_t* q;     // bf16 [B, H, N, d]
-  const uint16_t* k;
+  const uint16_t* k;     // bf16 [B, Hkv, N, d]
   const uint16_t* v;
   const uint16_t* dout;  // bf16 [B, H, N, d], upstream gradient
   const float* o;        // fp32 [B, H, N, d], forward output
   const float* lse;      // fp32 [B, H, N], forward logsumexp (natural log)
   float* delta;          // fp32 [B, H, N] workspace: rowsum(dO * O)
   float* dq;             // fp32 [B, H, N, d]
-  float* dk;
+  float* dk;             // fp32 [B, Hkv, N, d]
   float* dv;
   int B, H, N;
+  int Hkv;               // KV heads (H a multiple of Hkv); k, v are [B, Hkv, N, d]
   float scale;  // softmax scale
   float c;      // scale * log2(e)
   int split_dkdv;  // d = 128: dV and dK in two launches (set when the grid fills the device)

@@ -174,6 +174,24 @@ int fa_bwd_bf16(const void* q, const void* k, const void* v, const float* o, con
                 float softmax_scale, void* stream);
 
 /*
+ * fa_bwd_bf16_gqa -- the same backward for grouped- and multi-query heads
+ * (queries and keys of equal length N): the backward of fa_fwd_bf16_gqa
+ * with Nq = Nk = N.  Query head h reads KV head h / (Hq / Hkv), so a KV
+ * head's dK, dV are the sums of the gradients of the Hq / Hkv query heads
+ * that read it (the chain rule through the shared head).
+ *
+ *   q, dout       : bf16 [B, Hq, N, d]    k, v   : bf16 [B, Hkv, N, d]
+ *   o             : fp32 [B, Hq, N, d]    lse    : fp32 [B, Hq, N]
+ *   dq            : fp32 [B, Hq, N, d]    dk, dv : fp32 [B, Hkv, N, d]
+ *   delta_ws      : fp32 [B, Hq, N]       caller-owned workspace
+ *   Hq            : a multiple of Hkv (FA_ERR_SHAPE otherwise, or for Hkv < 1)
+ *   everything else as fa_bwd_bf16 (which is this call with Hkv = Hq).
+ */
+int fa_bwd_bf16_gqa(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
+                    float* dq, float* dk, float* dv, float* delta_ws, int B, int Hq, int Hkv, int N, int d,
+                    int causal, float softmax_scale, void* stream);
+
+/*
  * fa_fp8_prep -- one pass over one tensor that produces the FP8 operands of
  * fa_fwd_fp8 ("Incoherent Processing" and "Block Quantization" sections of
  * the FA3 explainer cited above; E4M3 largest value 448 from the wmrh.cn

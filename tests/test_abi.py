@@ -121,6 +121,14 @@ def test_bwd_validation(lib):
     assert f(ws=FAKE + 4) == -5
 
 
+def test_bwd_gqa_validation(lib):
+    f = lambda **kw: lib.fa_bwd_bf16_gqa(kw.get("q", FAKE), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1,
+                                         kw.get("Hq", 8), kw.get("Hkv", 2), 64, kw.get("d", 128), 0, 0.1, None)
+    assert f(q=None) == -1
+    assert f(Hkv=0) == -2 and f(Hq=6, Hkv=4) == -2 and f(Hq=0) == -2
+    assert f(d=256) == -3
+
+
 def test_valid_call_without_gpu_reports_device_error(lib):
     import torch
 

@@ -13,7 +13,7 @@ import torch
 
 import exact_attention_73_amd as fa
 from exact_attention_73_amd.inputs import WORKLOADS, make_do, make_qkv, softmax_scale
-from oracle import attention_bwd_ref
+from oracle import attention_bwd_ref, attention_gqa_bwd_ref
 from tests._util import errors
 
 pytestmark = pytest.mark.gpu
@@ -87,6 +87,66 @@ def test_bwd_split_launches_match_single_launch(causal):
     ref = attention_bwd_ref(q[1:2, 5:6].cpu(), k[1:2, 5:6].cpu(), v[1:2, 5:6].cpu(), do[1:2, 5:6].cpu(), causal=causal,
                             scale=softmax_scale(128))
     _check(tuple(g[1:2, 5:6].cpu().numpy() for g in big), ref, f"split launches causal={causal}")
+
+
+def _gqa_inputs(B, Hq, Hkv, N, d, seed):
+    q, _, _ = make_qkv(B, Hq, N, d, seed)
+    _, k, v = make_qkv(B, Hkv, N, d, seed + 1)
+    return q, k, v, make_do(B, Hq, N, d, seed)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,Hq,Hkv,N,d", [(1, 4, 2, 300, 128), (1, 6, 1, 129, 64), (2, 8, 2, 1000, 128),
+                                           (1, 4, 4, 200, 64), (1, 8, 1, 64, 128)])
+def test_bwd_gqa_against_oracle(B, Hq, Hkv, N, d, causal):
+    q, k, v, do = _gqa_inputs(B, Hq, Hkv, N, d, seed=6400 + N + d + Hq)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = fa.fwd_bf16_gqa(qd, kd, vd, causal=causal)
+    got = fa.bwd_bf16_gqa(qd, kd, vd, o, lse, dod, causal=causal)
+    torch.cuda.synchronize()
+    ref = attention_gqa_bwd_ref(q, k, v, do, causal=causal, scale=softmax_scale(d))
+    _check(tuple(g.cpu().numpy() for g in got), ref, f"gqa B{B} Hq{Hq} Hkv{Hkv} N{N} d{d} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_gqa_split_launches_sampled(causal):
+    # 4 x 8 KV heads x 8 key tiles = 256 workgroups: dK/dV take the two-launch path
+    B, Hq, Hkv, N, d = 4, 32, 8, 1000, 128
+    q, k, v, do = _gqa_inputs(B, Hq, Hkv, N, d, seed=6500)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = fa.fwd_bf16_gqa(qd, kd, vd, causal=causal)
+    dq, dk, dv = fa.bwd_bf16_gqa(qd, kd, vd, o, lse, dod, causal=causal)
+    torch.cuda.synchronize()
+    for b, hk in ((0, 0), (3, 5)):
+        hs = slice(4 * hk, 4 * hk + 4)
+        ref = attention_gqa_bwd_ref(q[b:b + 1, hs], k[b:b + 1, hk:hk + 1], v[b:b + 1, hk:hk + 1], do[b:b + 1, hs],
+                                    causal=causal, scale=softmax_scale(d))
+        got = (dq[b:b + 1, hs].cpu().numpy(), dk[b:b + 1, hk:hk + 1].cpu().numpy(), dv[b:b + 1, hk:hk + 1].cpu().numpy())
+        _check(got, ref, f"gqa split b={b} kv head={hk} causal={causal}")
+
+
+def test_bwd_gqa_consistent_with_expanded_heads():
+    # dQ equals the ungrouped backward on K, V copied to every query head (the
+    # same kernel work per query head: bit for bit); dK, dV equal the sums of
+    # the copies' gradients up to the order of the fp32 sums
+    B, Hq, Hkv, N, d = 1, 6, 2, 257, 128
+    q, k, v, do = (x.cuda() for x in _gqa_inputs(B, Hq, Hkv, N, d, seed=6600))
+    o, lse = fa.fwd_bf16_gqa(q, k, v, causal=True)
+    dq, dk, dv = fa.bwd_bf16_gqa(q, k, v, o, lse, do, causal=True)
+    ke, ve = (x.repeat_interleave(Hq // Hkv, dim=1).contiguous() for x in (k, v))
+    dq1, dk1, dv1 = fa.bwd_bf16(q, ke, ve, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq1)
+    for g, g1 in ((dk, dk1), (dv, dv1)):
+        s = g1.reshape(B, Hkv, Hq // Hkv, N, d).sum(2)
+        assert float((g - s).abs().max()) <= 1e-4 * float(s.abs().max())
+    # one group per KV head is the ungrouped backward exactly
+    q2, k2, v2 = q[:, :2].contiguous(), k, v
+    o2, l2 = fa.fwd_bf16(q2, k2, v2, causal=True)
+    a = fa.bwd_bf16_gqa(q2, k2, v2, o2, l2, do[:, :2].contiguous(), causal=True)
+    b_ = fa.bwd_bf16(q2, k2, v2, o2, l2, do[:, :2].contiguous(), causal=True)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(a, b_))
 
 
 def test_bwd_deterministic():
