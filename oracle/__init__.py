@@ -22,6 +22,8 @@ Modules:
   materialised) and ``online_ref`` (the tiled online-softmax recurrence).
 * :mod:`oracle.gqa` -- ``attention_gqa_ref`` (grouped/multi-query heads,
   unequal query and key lengths, bottom-right causal alignment).
+* :mod:`oracle.varlen` -- ``attention_varlen_ref`` (sequences of different
+  lengths packed end to end, token-major layout).
 * :mod:`oracle.backward` -- ``attention_bwd_ref`` (dQ, dK, dV of the
   definition, written out) and ``attention_gqa_bwd_ref`` (grouped heads:
   each KV head's gradient summed over the query heads that read it).
@@ -38,6 +40,7 @@ marked "parity unpinned" in :mod:`oracle.fp8`.
 from .attention import attention_ref, online_ref  # noqa: F401
 from .backward import attention_bwd_ref, attention_gqa_bwd_ref  # noqa: F401
 from .gqa import attention_gqa_ref  # noqa: F401
+from .varlen import attention_varlen_ref  # noqa: F401
 from .fp8 import (  # noqa: F401
     E4M3_MAX,
     e4m3_decode,
