@@ -26,6 +26,7 @@ _VP, _FP, _I, _F, _LL = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c
 SIGNATURES = {
     "fa_fwd_bf16": (_I, [_VP, _VP, _VP, _FP, _FP, _I, _I, _I, _I, _I, _F, _VP]),
     "fa_fwd_bf16_gqa": (_I, [_VP, _VP, _VP, _FP, _FP, _I, _I, _I, _I, _I, _I, _I, _F, _VP]),
+    "fa_fwd_bf16_varlen": (_I, [_VP, _VP, _VP, _FP, _FP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _I, _F, _VP]),
     "fa_fwd_bf16_decode_splits": (_I, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "fa_fwd_bf16_decode_workspace": (_LL, [_I, _I, _I, _I, _I]),
     "fa_fwd_bf16_decode": (_I, [_VP, _VP, _VP, _FP, _FP, _I, _I, _I, _I, _I, _I, _I, _F, _I, _VP, _LL, _VP]),
@@ -123,6 +124,34 @@ def _gqa_shapes(q, k, v):
         raise ValueError("q must be [B, Hq, Nq, d] and k, v [B, Hkv, Nk, d]")
     B, Hq, Nq, d = q.shape
     return B, Hq, k.shape[1], Nq, k.shape[2], d
+
+
+def fwd_bf16_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal: bool = False,
+                    softmax_scale: float | None = None, out=None, lse=None):
+    """Forward over packed sequences: q ``[total_q, Hq, d]``, k, v
+    ``[total_k, Hkv, d]`` (bf16), ``cu_seqlens_*`` int32 ``[B + 1]`` on the
+    GPU.  Returns fp32 ``o [total_q, Hq, d]`` and ``lse [Hq, total_q]``."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, n)
+    _need(cu_seqlens_q, torch.int32, "cu_seqlens_q")
+    _need(cu_seqlens_k, torch.int32, "cu_seqlens_k")
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or k.shape[2] != q.shape[2]:
+        raise ValueError("q must be [total_q, Hq, d] and k, v [total_k, Hkv, d]")
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_k.shape != cu_seqlens_q.shape or cu_seqlens_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must be [B + 1]")
+    total_q, Hq, d = q.shape
+    total_k, Hkv = k.shape[0], k.shape[1]
+    B = cu_seqlens_q.numel() - 1
+    scale = (1.0 / d ** 0.5) if softmax_scale is None else float(softmax_scale)
+    o = torch.empty((total_q, Hq, d), dtype=torch.float32, device=q.device) if out is None else out
+    ls = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(o, torch.float32, "out")
+    _need(ls, torch.float32, "lse")
+    st = load().fa_fwd_bf16_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), ls.data_ptr(),
+                                   cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, Hq, Hkv, total_q, total_k,
+                                   int(max_seqlen_q), d, int(bool(causal)), scale, _stream(q))
+    _check("fa_fwd_bf16_varlen", st)
+    return o, ls
 
 
 def decode_splits(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, num_splits: int = 0,

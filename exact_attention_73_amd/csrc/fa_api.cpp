@@ -175,6 +175,44 @@ int fa_fwd_bf16_gqa(const void* q, const void* k, const void* v, float* o, float
   return launch_status(fa::launch_fwd_bf16(p, d, causal == 1, static_cast<hipStream_t>(stream)));
 }
 
+int fa_fwd_bf16_varlen(const void* q, const void* k, const void* v, float* o, float* lse, const int* cu_seqlens_q,
+                       const int* cu_seqlens_k, int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                       int d, int causal, float softmax_scale, void* stream) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULL_PTR;
+  const bool dok = d == 64 || d == 128 || d == 256;
+  const double dd = dok ? d : 1;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || total_q < 0 || total_k < 0 || max_seqlen_q < 0) return FA_ERR_SHAPE;
+  // K/V rows of one sequence are addressed with 32-bit byte offsets
+  if ((double)total_k * Hkv * dd * 2.0 >= 2147483648.0) return FA_ERR_SHAPE;
+  if ((double)total_q * Hq * dd >= 1099511627776.0) return FA_ERR_SHAPE;  // 2^40 elements
+  if ((double)B * Hq * (((double)max_seqlen_q + 127) / 128) >= 2147483647.0) return FA_ERR_SHAPE;
+  if (!dok) return FA_ERR_HEADDIM;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (int e = check_scale(softmax_scale)) return e;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens_q) | reinterpret_cast<uintptr_t>(cu_seqlens_k)) & 3u) return FA_ERR_ALIGN;
+  if (int e = check_device()) return e;
+
+  fa::FwdBf16Params p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.H = Hq;
+  p.N = max_seqlen_q;
+  p.Hkv = Hkv;
+  p.Nk = 0;
+  p.scale = softmax_scale;
+  p.c = softmax_scale * 1.4426950408889634f;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.total_q = total_q;
+  p.total_k = total_k;
+  return launch_status(fa::launch_fwd_bf16_varlen(p, d, causal == 1, static_cast<hipStream_t>(stream)));
+}
+
 int fa_fwd_bf16_decode_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits, int num_cus) {
   if (int e = check_decode_shape(B, Hq, Hkv, Nq, Nk, d)) return e;
   if (num_splits < 0 || num_cus < 0 || (num_splits == 0 && num_cus < 1)) return FA_ERR_ARG;

@@ -156,7 +156,7 @@ __device__ __forceinline__ void schedule_step() {
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, Bf16Cfg<D>::MINB) void fwd_bf16_kernel(FwdBf16Params p) {
   using Cfg = Bf16Cfg<D>;
   constexpr int QB = Cfg::QB, NW = Cfg::NW, BC = Cfg::BC;
@@ -181,11 +181,8 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, Bf16Cfg<D>::MINB) void fwd_bf1
   __shared__ __attribute__((aligned(1024))) uint16_t Vs0[BC * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Vs1[BC * D];
 
-  const int N = p.N;    // queries
-  const int Nk = p.Nk;  // keys
-  const int off = Nk - N;  // causal alignment: query i sees keys j <= i + off
   const int BH = p.B * p.H;
-  const int nq = (N + BR - 1) / BR;
+  const int nq = (p.N + BR - 1) / BR;  // query tiles (of the longest sequence when VARLEN)
   int bh, qt;
   if constexpr (CAUSAL) {
     // heaviest query tiles first; heads vary fastest so every XCD gets a mix
@@ -196,13 +193,41 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, Bf16Cfg<D>::MINB) void fwd_bf1
     bh = w / nq;
     qt = w % nq;
   }
+  // KV head of this query head: each KV head serves H / Hkv consecutive query heads
+  const int bb = bh / p.H, hh = bh - bb * p.H;
+  const int hk = hh / (p.H / p.Hkv);
+
+  // Per-sequence extents.  Fixed-length batch: [B, H, N, d] and [B, Hkv, Nk, d],
+  // rows d apart.  Packed batch: sequence bb's rows of the token-major tensors,
+  // H d (q, o) and Hkv d (k, v) apart, bounds clamped into the tensors.
+  int N, Nk;
+  size_t qbase, kvbase;  // element offsets of row 0 of this (sequence, head)
+  int qstride, kvstride;  // elements between consecutive rows
+  size_t lbase;           // lse index of row 0
+  if constexpr (VARLEN) {
+    const int q0s = min(max(p.cu_q[bb], 0), p.total_q), q1s = min(max(p.cu_q[bb + 1], q0s), p.total_q);
+    const int k0s = min(max(p.cu_k[bb], 0), p.total_k), k1s = min(max(p.cu_k[bb + 1], k0s), p.total_k);
+    N = q1s - q0s;
+    Nk = k1s - k0s;
+    if (qt * BR >= N) return;  // past this sequence's queries: the whole workgroup leaves
+    qstride = p.H * D;
+    kvstride = p.Hkv * D;
+    qbase = (size_t)q0s * qstride + (size_t)hh * D;
+    kvbase = (size_t)k0s * kvstride + (size_t)hk * D;
+    lbase = (size_t)hh * p.total_q + q0s;
+  } else {
+    N = p.N;
+    Nk = p.Nk;
+    qstride = D;
+    kvstride = D;
+    qbase = (size_t)bh * N * D;
+    kvbase = ((size_t)bb * p.Hkv + hk) * Nk * D;
+    lbase = (size_t)bh * N;
+  }
+  const int off = Nk - N;  // causal alignment: query i sees keys j <= i + off
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const size_t base = (size_t)bh * N * D;  // q, o
-  // KV head of this query head: each KV head serves H / Hkv consecutive query heads
-  const int bb = bh / p.H, hh = bh - bb * p.H;
-  const size_t kvbase = ((size_t)bb * p.Hkv + hh / (p.H / p.Hkv)) * Nk * D;
   const int q0 = qt * BR + wave * QW;  // first query row of this wave
   int qrow[QB];                        // the query rows this lane owns
 #pragma unroll
@@ -214,7 +239,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, Bf16Cfg<D>::MINB) void fwd_bf1
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const bool ok = qrow[qb] < N;
-    const u32x4* src = reinterpret_cast<const u32x4*>(p.q + base + (size_t)(ok ? qrow[qb] : 0) * D);
+    const u32x4* src = reinterpret_cast<const u32x4*>(p.q + qbase + (size_t)(ok ? qrow[qb] : 0) * qstride);
 #pragma unroll
     for (int s = 0; s < NQS; ++s) {
       const u32x4 t = ok ? src[2 * s + hi] : u32x4{0, 0, 0, 0};
@@ -229,18 +254,22 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, Bf16Cfg<D>::MINB) void fwd_bf1
   // Wave-load i of wave w fills LDS bytes [(IPW w + i) KB, +1 KB) of the
   // slot: RPI rows; lane L writes physical chunk L % CPR of row L / CPR and
   // therefore fetches the logical chunk that the swizzle puts there.
-  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(p.k + kvbase, Nk * ROWB);
-  const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(p.v + kvbase, Nk * ROWB);
+  // The buffer range ends with this head's last key row, so rows past Nk
+  // (also the next sequence's rows in a packed batch) read as zero.
+  const int kvrowb = kvstride * 2;  // bytes between K/V rows in memory
+  const int kvbytes = Nk > 0 ? (Nk - 1) * kvrowb + ROWB : 0;
+  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(p.k + kvbase, kvbytes);
+  const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(p.v + kvbase, kvbytes);
   int koff[IPW], voff[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
     const int row = (wave * IPW + i) * RPI + lane / CPR, pc = lane % CPR;
-    koff[i] = row * ROWB + ((pc ^ k_swizzle<D>(row)) * 16);
-    voff[i] = row * ROWB + ((pc ^ v_swizzle<D>(row)) * 16);
+    koff[i] = row * kvrowb + ((pc ^ k_swizzle<D>(row)) * 16);
+    voff[i] = row * kvrowb + ((pc ^ v_swizzle<D>(row)) * 16);
   }
   auto issue = [&](const __amdgpu_buffer_rsrc_t& r, uint16_t* dst, const int (&off)[IPW], int j) {
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) lds_dma16(r, dst + (wave * IPW + i) * 512, off[i] + j * BC * ROWB);
+    for (int i = 0; i < IPW; ++i) lds_dma16(r, dst + (wave * IPW + i) * 512, off[i] + j * BC * kvrowb);
   };
 
   // S^T = K Q^T: each K operand (row kb*32 + l32, chunk 2 st + hi) feeds QB products
@@ -412,7 +441,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, Bf16Cfg<D>::MINB) void fwd_bf1
     if (qrow[qb] < N) {
       // a row that sees no key (only when N > Nk, causal) has l = 0: O = 0, lse = -inf
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      float* orow = p.o + base + (size_t)qrow[qb] * D;
+      float* orow = p.o + qbase + (size_t)qrow[qb] * qstride;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -421,29 +450,39 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, Bf16Cfg<D>::MINB) void fwd_bf1
                              o[qb][db][4 * g + 3] * inv};
           *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * g + 4 * hi) = val;
         }
-      if (hi == 0) p.lse[(size_t)bh * N + qrow[qb]] = m_run[qb] * p.scale + __logf(l_tot);
+      if (hi == 0) p.lse[lbase + qrow[qb]] = m_run[qb] * p.scale + __logf(l_tot);
     }
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch(const FwdBf16Params& p, hipStream_t stream) {
   constexpr int BR = rows_per_workgroup<D>();
   const int nq = (p.N + BR - 1) / BR;
   const unsigned grid = (unsigned)nq * (unsigned)p.B * (unsigned)p.H;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(grid), dim3(Bf16Cfg<D>::NW * 64), 0, stream, p);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, VARLEN>), dim3(grid), dim3(Bf16Cfg<D>::NW * 64), 0, stream, p);
   return hipGetLastError();
+}
+
+template <bool VARLEN>
+hipError_t launch_any(const FwdBf16Params& p, int d, bool causal, hipStream_t stream) {
+  switch (d) {
+    case 64: return causal ? launch<64, true, VARLEN>(p, stream) : launch<64, false, VARLEN>(p, stream);
+    case 128: return causal ? launch<128, true, VARLEN>(p, stream) : launch<128, false, VARLEN>(p, stream);
+    case 256: return causal ? launch<256, true, VARLEN>(p, stream) : launch<256, false, VARLEN>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdBf16Params& p, int d, bool causal, hipStream_t stream) {
-  switch (d) {
-    case 64: return causal ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
-    case 128: return causal ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
-    case 256: return causal ? launch<256, true>(p, stream) : launch<256, false>(p, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return launch_any<false>(p, d, causal, stream);
+}
+
+hipError_t launch_fwd_bf16_varlen(const FwdBf16Params& p, int d, bool causal, hipStream_t stream) {
+  return launch_any<true>(p, d, causal, stream);
 }
 
 }  // namespace fa

@@ -18,9 +18,16 @@ struct FwdBf16Params {
   int Hkv, Nk;   // KV heads (H a multiple of Hkv) and keys; query i sees keys j <= i + Nk - N when causal
   float scale;   // softmax scale
   float c;       // scale * log2(e)
+  // packed variable-length batch (launch_fwd_bf16_varlen): q, o [total_q, H, d],
+  // k, v [total_k, Hkv, d], lse [H, total_q]; sequence b owns rows cu_q[b] ..
+  // cu_q[b+1] - 1 and cu_k[b] .. cu_k[b+1] - 1; B sequences, N = longest query count
+  const int* cu_q = nullptr;
+  const int* cu_k = nullptr;
+  int total_q = 0, total_k = 0;
 };
 
 hipError_t launch_fwd_bf16(const FwdBf16Params& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_fwd_bf16_varlen(const FwdBf16Params& p, int d, bool causal, hipStream_t stream);
 
 struct DecBf16Params {
   const uint16_t* q;  // bf16 [B, Hq, Nq, d]

@@ -100,6 +100,35 @@ int fa_fwd_bf16_gqa(const void* q, const void* k, const void* v, float* o, float
                     int Nq, int Nk, int d, int causal, float softmax_scale, void* stream);
 
 /*
+ * fa_fwd_bf16_varlen -- the forward over a batch of sequences of different
+ * lengths packed end to end (the FA3 explainer names variable-length
+ * batches among the shapes kernels are dispatched on, section "安装了包，
+ * 为什么可能没有用上 FA3", and asks tests to cover very short and empty
+ * ranges in them, section "正确性验证要覆盖异步边界").
+ *
+ *   q        : bf16 [total_q, Hq, d]    k, v : bf16 [total_k, Hkv, d]  (token-major)
+ *   o        : fp32 [total_q, Hq, d]    lse  : fp32 [Hq, total_q]
+ *   cu_seqlens_q, cu_seqlens_k : int32 [B + 1] DEVICE arrays, nondecreasing
+ *              from 0 to total_q (total_k): sequence b owns query rows
+ *              cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1 and key rows
+ *              cu_seqlens_k[b] .. cu_seqlens_k[b+1] - 1.  Values are clamped
+ *              into [0, total] on the device, so no access leaves the tensors.
+ *   max_seqlen_q : at least the largest query count of any sequence (sizes
+ *              the grid; query rows beyond it are not written).
+ *   Hq, Hkv, d, causal, softmax_scale : as fa_fwd_bf16_gqa, applied to each
+ *              sequence on its own (causal bottom-right per sequence; a query
+ *              that sees no key, e.g. in a sequence with no keys, gets o = 0
+ *              and lse = -inf).  Empty sequences are allowed.
+ *
+ * Rows of o and lse that belong to no sequence are not written.
+ * FA_ERR_SHAPE also when total_k * Hkv * d * 2 >= 2^31 or a size is negative;
+ * FA_ERR_ALIGN when a cu_seqlens array is not 4-byte aligned.
+ */
+int fa_fwd_bf16_varlen(const void* q, const void* k, const void* v, float* o, float* lse, const int* cu_seqlens_q,
+                       const int* cu_seqlens_k, int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                       int d, int causal, float softmax_scale, void* stream);
+
+/*
  * Decode-shaped forward: a few queries per head against a long key/value
  * sequence.  The FA3 explainer (sections "GQA/MQA 为何改变 Kernel 任务数量"
  * and "Prefill、Decode 和训练的收益不同") names split-KV and packing the

@@ -82,6 +82,18 @@ def test_gqa_validation(lib):
     assert f(d=96) == -3 and f(causal=2) == -4
 
 
+def test_varlen_validation(lib):
+    f = lambda **kw: lib.fa_fwd_bf16_varlen(kw.get("q", FAKE), FAKE, FAKE, FAKE, FAKE, kw.get("cq", FAKE), FAKE,
+                                            kw.get("B", 2), kw.get("Hq", 8), kw.get("Hkv", 2), kw.get("tq", 100),
+                                            kw.get("tk", 100), kw.get("mq", 64), kw.get("d", 128),
+                                            kw.get("causal", 0), 0.1, None)
+    assert f(q=None) == -1 and f(cq=None) == -1
+    assert f(B=0) == -2 and f(Hq=6, Hkv=4) == -2 and f(tq=-1) == -2 and f(mq=-1) == -2
+    assert f(tk=1 << 20, Hkv=8, Hq=8) == -2  # total_k * Hkv * d * 2 >= 2^31
+    assert f(d=96) == -3 and f(causal=3) == -4
+    assert f(cq=FAKE + 2) == -5
+
+
 def test_decode_splits_and_workspace(lib):
     sp = lambda B=1, Hq=32, Hkv=8, Nq=1, Nk=131072, d=128, n=0, cus=256: lib.fa_fwd_bf16_decode_splits(
         B, Hq, Hkv, Nq, Nk, d, n, cus)
