@@ -53,7 +53,7 @@ TRAFFIC_SOURCES = ("exact_attention_73_amd/csrc/fa_fwd_bf16.hip", "exact_attenti
 COPY_CALIBRATION_BYTES = 256 << 20
 
 
-ALL_LEGS = ("sweep", "sweep64", "sweep256", "long", "fp8", "bwd", "decode")
+ALL_LEGS = ("sweep", "sweep64", "sweep256", "long", "fp8", "bwd", "decode", "varlen")
 
 
 def fwd_bytes(B, H, N, d):
@@ -365,6 +365,32 @@ def main():
                 "prefill_kernel_same_shape_us": round(sp["mean"] * 1e6, 1)}
             del qd_, kd_, vd_, od_, ld_, wsd
         legs["bf16_decode"] = dec
+
+    if "varlen" in legs_on:
+        # 16 causal sequences of mixed lengths (seeded, 256..4096 keys) packed
+        # end to end; FLOPs count each sequence's own work only.  The same
+        # batch padded to its longest sequence is timed beside it.
+        g = torch.Generator("cpu").manual_seed(73800)
+        lens = [int(x) for x in torch.randint(256, 4097, (16,), generator=g)]
+        Hv, dv_ = 16, 128
+        tot = sum(lens)
+        qv_, _, _ = make_qkv(1, Hv, tot, dv_, 73801)
+        _, kv_, vv_ = make_qkv(1, Hv, tot, dv_, 73802)
+        qv_, kv_, vv_ = (x[0].transpose(0, 1).contiguous().to(dev) for x in (qv_, kv_, vv_))
+        cu = torch.tensor([0] + lens, dtype=torch.int32).cumsum(0).to(torch.int32).to(dev)
+        ov_ = torch.empty((tot, Hv, dv_), dtype=torch.float32, device=dev)
+        lv_ = torch.empty((Hv, tot), dtype=torch.float32, device=dev)
+        st = _time_launches(lambda: fa.fwd_bf16_varlen(qv_, kv_, vv_, cu, cu, max(lens), causal=True, out=ov_,
+                                                       lse=lv_), 20, 5)
+        fl = sum(4.0 * Hv * n * n * dv_ / 2 for n in lens)
+        Np = max(lens)
+        qp, kp, vp = (torch.zeros((16, Hv, Np, dv_), dtype=torch.bfloat16, device=dev) for _ in range(3))
+        sp = _time_launches(lambda: fa.fwd_bf16(qp, kp, vp, causal=True), 10, 3)
+        legs["bf16_varlen"] = {
+            "workload": f"16 sequences, {tot} tokens (lengths 256..4096, seeded), H16 d128 causal",
+            "tflops": round(fl / st["mean"] / 1e12, 1), "frac": round(fl / st["mean"] / 1e12 / PEAK_BF16, 4),
+            "us": round(st["mean"] * 1e6, 1), "padded_to_longest_us": round(sp["mean"] * 1e6, 1)}
+        del qv_, kv_, vv_, ov_, lv_, qp, kp, vp
 
     if args.copy_calibration:
         src = torch.ones(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
