@@ -229,7 +229,7 @@ __global__ __launch_bounds__(DecCfg<D>::NW * 64, DecCfg<D>::MINB) void dec_bf16_
     float mx = -INFINITY;
 #pragma unroll
     for (int rr = 0; rr < 16; rr += 2) mx = fmax3(mx, s[rr], s[rr + 1]);
-    mx = __builtin_fmaxf(mx, swap_halves(mx));
+    mx = max_halves(mx);
     // online softmax update; a row that has seen no key yet keeps m = -inf,
     // l = 0, O = 0 (and takes alpha = 1 rather than exp2(-inf - -inf))
     const float m_new = __builtin_fmaxf(m_run, mx);
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(DecCfg<D>::NW * 64, DecCfg<D>::MINB) void dec_bf16_
   if (i < n_my) step(i, S0);
 
   // ---- merge the NW waves through LDS (slot 0 reused) ---------------------
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = sum_halves(l_run);
   wait_vmem<0>();   // the trailing zero loads into the ring have landed
   __syncthreads();  // and every wave has finished with its ring
   float* ml = reinterpret_cast<float*>(S0);  // [NW][64]: m of 32 rows, then l

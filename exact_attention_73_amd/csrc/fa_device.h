@@ -42,9 +42,20 @@ __device__ __forceinline__ f32x16 mfma_fp8_32x32x64(i32x8 a, i32x8 b, f32x16 c, 
 // 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Value of the lane with index L ^ 32 (the other half of the wave).
-__device__ __forceinline__ float swap_halves(float x) {
-  return __shfl_xor(x, 32, 64);
+// Combine lane L's value with lane L ^ 32's (the other half of the wave)
+// without a trip through LDS: v_permlane32_swap exchanges lanes 32..63 of its
+// first operand with lanes 0..31 of its second, so with x in both, the two
+// results hold x[L] and x[L ^ 32] in every lane (which one is which depends on
+// the half; max and + do not care, and give the same bits in both halves).
+__device__ __forceinline__ float max_halves(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ float fmax3(float a, float b, float c) { return __builtin_fmaxf(__builtin_fmaxf(a, b), c); }

@@ -434,7 +434,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) m = fmax3(m, sv[kb][r], sv[kb][r + 1]);
-    return __builtin_fmaxf(m, swap_halves(m));
+    return max_halves(m);
   };
 
   // mx: raw row max of s_in on entry, of s_out on exit (taken at the end of
@@ -543,7 +543,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
     if (j + 1 < ntiles) step(j + 1, sb, sa, mx, Ks1, Ks0, Vs1, Vs0);
   }
 
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = sum_halves(l_run);
   if (qrow < N) {
     const float inv = 1.f / l_tot;
     float* orow = p.o + (size_t)bh * N * D + (size_t)qrow * D;

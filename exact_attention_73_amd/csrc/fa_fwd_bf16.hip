@@ -310,7 +310,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, Bf16Cfg<D>::MINB) void fwd_bf1
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) mx = fmax3(mx, s[kb][r], s[kb][r + 1]);
-    return __builtin_fmaxf(mx, swap_halves(mx));
+    return max_halves(mx);
   };
 
   float m_run[QB], l_run[QB];  // exponent reference (raw score units), this half-wave's row sum
@@ -437,7 +437,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, Bf16Cfg<D>::MINB) void fwd_bf1
   // ---- epilogue: O / l, lse = m * scale + ln l ----------------------------
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = l_run[qb] + swap_halves(l_run[qb]);
+    const float l_tot = sum_halves(l_run[qb]);
     if (qrow[qb] < N) {
       // a row that sees no key (only when N > Nk, causal) has l = 0: O = 0, lse = -inf
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;

@@ -41,10 +41,18 @@ __global__ void k_cvt_fp8(const float* x, uint32_t* out, int n) {
   out[i] = w;
 }
 
-// x: 64 floats -> y[l] = x[l ^ 32] via the shuffle the kernels use
+// x: 64 floats -> y: 4 x 64 floats: the two results of v_permlane32_swap
+// with x in both operands, then their max and their sum (the half-wave row
+// max and row sum the kernels take)
 __global__ void k_swap_halves(const float* x, float* y) {
   const int l = threadIdx.x;
-  y[l] = __shfl_xor(x[l], 32, 64);
+  const unsigned u = __float_as_uint(x[l]);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  y[l] = a;
+  y[64 + l] = b;
+  y[128 + l] = __builtin_fmaxf(a, b);
+  y[192 + l] = a + b;
 }
 
 // transposed LDS read: LDS holds u16 values 0..1023; lane l reads at byte

@@ -166,11 +166,21 @@ def test_cvt_pk_fp8_rounding_matches_oracle(probes):
 
 
 def test_swap_halves(probes):
-    x = torch.arange(64, dtype=torch.float32, device="cuda")
-    y = torch.zeros(64, dtype=torch.float32, device="cuda")
+    # v_permlane32_swap: lanes 32..63 of the first operand trade places with
+    # lanes 0..31 of the second; max and sum of the two results combine each
+    # lane's value with the other half-wave's, bit-identically in both halves
+    xh = (np.arange(64, dtype=np.float32) * 1.37 - 40.0).astype(np.float32)
+    xh[[3, 40]] = [1e-3, -7.25]
+    x = torch.from_numpy(xh).cuda()
+    y = torch.zeros(4 * 64, dtype=torch.float32, device="cuda")
     assert probes.probe_swap_halves(_p(x), _p(y), _s()) == 0
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(y.cpu().numpy(), np.arange(64) ^ 32)
+    a, b, mx, sm = y.cpu().numpy().reshape(4, 64)
+    lane = np.arange(64)
+    np.testing.assert_array_equal(a, np.where(lane < 32, xh, xh[lane ^ 32]))
+    np.testing.assert_array_equal(b, np.where(lane < 32, xh[lane ^ 32], xh))
+    np.testing.assert_array_equal(mx, np.maximum(xh, xh[lane ^ 32]))
+    np.testing.assert_array_equal(sm, (xh + xh[lane ^ 32]).astype(np.float32))
 
 
 def test_ds_read_tr16_b64_mapping(probes):
