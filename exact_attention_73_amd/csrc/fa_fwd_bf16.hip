@@ -435,22 +435,55 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, Bf16Cfg<D>::MINB) void fwd_bf1
   }
 
   // ---- epilogue: O / l, lse = m * scale + ln l ----------------------------
+  // A lane holds 16-byte pieces of ONE output row, so storing straight from
+  // the accumulators writes 32 bytes into each of 32 rows per instruction.
+  // Where a wave's fp32 tile fits one ring slot (d = 64, 128), it goes
+  // through LDS first (16-byte chunks XOR-swizzled by row: conflict-free on
+  // both sides) and leaves as whole rows, 1 KB of consecutive bytes per
+  // instruction.
+  constexpr int CPO = D / 4;  // 16-byte chunks per fp32 output row
+  constexpr bool kStageO = QB == 1 && 32 * D * 4 <= BC * D * 2;
+  float inv[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = sum_halves(l_run[qb]);
-    if (qrow[qb] < N) {
-      // a row that sees no key (only when N > Nk, causal) has l = 0: O = 0, lse = -inf
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      float* orow = p.o + qbase + (size_t)qrow[qb] * qstride;
+    // a row that sees no key (only when N > Nk, causal) has l = 0: O = 0, lse = -inf
+    inv[qb] = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qrow[qb] < N && hi == 0) p.lse[lbase + qrow[qb]] = m_run[qb] * p.scale + __logf(l_tot);
+  }
+  if constexpr (kStageO) {
+    __syncthreads();  // every wave is done with the ring (no tile loads are in flight)
+    float* st = reinterpret_cast<float*>(wave == 0 ? Ks0 : wave == 1 ? Ks1 : wave == 2 ? Vs0 : Vs1);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 val = {o[qb][db][4 * g] * inv, o[qb][db][4 * g + 1] * inv, o[qb][db][4 * g + 2] * inv,
-                             o[qb][db][4 * g + 3] * inv};
-          *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * g + 4 * hi) = val;
-        }
-      if (hi == 0) p.lse[lbase + qrow[qb]] = m_run[qb] * p.scale + __logf(l_tot);
+      for (int g = 0; g < 4; ++g) {
+        const int c = 8 * db + 2 * g + hi;  // chunk of d = 32 db + 8 g + 4 hi .. +3
+        const f32x4 val = {o[0][db][4 * g] * inv[0], o[0][db][4 * g + 1] * inv[0], o[0][db][4 * g + 2] * inv[0],
+                           o[0][db][4 * g + 3] * inv[0]};
+        *reinterpret_cast<f32x4*>(st + l32 * D + ((c ^ (l32 & (CPO - 1))) * 4)) = val;
+      }
+    constexpr int RPS = 64 / CPO;  // rows per store instruction
+#pragma unroll
+    for (int t = 0; t < 32 / RPS; ++t) {
+      const int r = t * RPS + lane / CPO, c = lane % CPO;
+      const f32x4 val = *reinterpret_cast<const f32x4*>(st + r * D + ((c ^ (r & (CPO - 1))) * 4));
+      if (q0 + r < N) *reinterpret_cast<f32x4*>(p.o + qbase + (size_t)(q0 + r) * qstride + 4 * c) = val;
+    }
+  } else {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (qrow[qb] < N) {
+        float* orow = p.o + qbase + (size_t)qrow[qb] * qstride;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 val = {o[qb][db][4 * g] * inv[qb], o[qb][db][4 * g + 1] * inv[qb],
+                               o[qb][db][4 * g + 2] * inv[qb], o[qb][db][4 * g + 3] * inv[qb]};
+            *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * g + 4 * hi) = val;
+          }
+      }
     }
   }
 }
