@@ -66,7 +66,7 @@ constexpr float kLazyLog2 = 8.f;  // rescale only when a row max grows by more t
 // wave unable to hide its own latencies.
 template <int D> struct Bf16Cfg;
 template <> struct Bf16Cfg<64> {
-  static constexpr int QB = 1, NW = 4, BC = 64, MINB = 2;
+  static constexpr int QB = 1, NW = 4, BC = 64, MINB = 3;
 };
 template <> struct Bf16Cfg<128> {
   static constexpr int QB = 1, NW = 4, BC = 64, MINB = 2;
@@ -75,6 +75,13 @@ template <> struct Bf16Cfg<256> {
   static constexpr int QB = 1, NW = 4, BC = 32, MINB = 1;
 };
 template <int D> constexpr int rows_per_workgroup() { return Bf16Cfg<D>::NW * 32 * Bf16Cfg<D>::QB; }
+// Workgroups per CU the register budget is cut for.  At d = 64 a wave issues
+// about as much vector work (exps, casts, sums) as matrix work per tile, so a
+// third wave per SIMD hides the latency two leave open; the packed-batch
+// variant keeps two (its extra sequence bookkeeping does not fit 168 VGPRs).
+template <int D, bool VARLEN> constexpr int min_blocks() {
+  return VARLEN && Bf16Cfg<D>::MINB > 2 ? 2 : Bf16Cfg<D>::MINB;
+}
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -157,7 +164,7 @@ __device__ __forceinline__ void schedule_step() {
 }
 
 template <int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, Bf16Cfg<D>::MINB) void fwd_bf16_kernel(FwdBf16Params p) {
+__global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, (min_blocks<D, VARLEN>())) void fwd_bf16_kernel(FwdBf16Params p) {
   using Cfg = Bf16Cfg<D>;
   constexpr int QB = Cfg::QB, NW = Cfg::NW, BC = Cfg::BC;
   constexpr int QW = 32 * QB;                 // query rows per wave

@@ -89,6 +89,32 @@ def test_prep_codes_and_scales(gpu_lib, N, mode):
                                   e4m3_decode(vc_ref))
 
 
+@pytest.mark.parametrize("mode", ["block+had", "tensor"])
+def test_prep_many_blocks_ragged(gpu_lib, mode):
+    """9 heads x 129 blocks = 1161 blocks (the last one of each head 37 rows
+    long): more blocks than the device holds prep workgroups at once, so the
+    grid runs in several rounds over blocks of different heads.  Q/K codes as
+    in the small cases, V bit-equal."""
+    B, H, N, d = 1, 9, 16421, 128
+    q, _, v = make_qkv(B, H, N, d, seed=4242, outliers=True)
+    signs = make_signs(H, d, seed=4243)
+    rot = mode == "block+had"
+    per_tensor = mode == "tensor"
+    x8, sc = fa.fp8_prep(q.cuda(), signs=signs.cuda() if rot else None, per_tensor=per_tensor)
+    codes_ref, s_ref, _ = quantize_fp8(q, signs=signs.numpy() if rot else None, per_tensor=per_tensor)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(sc.cpu().numpy(), s_ref.astype(np.float32), rtol=4 * 2.0 ** -23)
+    _codes_close(x8.cpu().numpy(), codes_ref, f"prep {mode} N={N} H={H}")
+    v8t, vs = fa.fp8_prep_v(v.cuda(), per_tensor=per_tensor)
+    vc_ref, vs_ref, _ = quantize_fp8(v, per_tensor=per_tensor, pow2=True)
+    torch.cuda.synchronize()
+    vt = unpermute_vt(v8t.cpu().numpy())
+    assert np.all(vt[..., N:] == 0)
+    np.testing.assert_array_equal(vs.cpu().numpy(), vs_ref.astype(np.float32))
+    np.testing.assert_array_equal(e4m3_decode(np.ascontiguousarray(np.swapaxes(vt[..., :N], 2, 3))),
+                                  e4m3_decode(vc_ref))
+
+
 def _fp8_pipeline(q, k, v, signs, mode, causal):
     rot = mode == "block+had"
     per_tensor = mode == "tensor"
