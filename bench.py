@@ -428,7 +428,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "fwd_bf16_kernel<128, non-causal>",
+            "kernel": "fwd_bf16_pp_kernel<non-causal> (d = 128 ping-pong)",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16,
             "unit": "TFLOP/s",

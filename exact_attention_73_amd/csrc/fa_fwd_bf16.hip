@@ -50,6 +50,12 @@
 // workgroup only visits key tiles up to its last query row, only tiles that
 // cross a wave's diagonal are masked element-wise, waves whose rows all lie
 // above a tile skip its products, and the heaviest query tiles launch first.
+//
+// d = 128 batches of 1024 or more query rows run a second kernel,
+// fwd_bf16_pp_kernel (below): eight waves per workgroup in two groups that
+// take turns on each SIMD's matrix core (one group's products while the
+// other group's softmax), the FA3 explainer's ping-pong scheduling mapped to
+// wave pairs of a SIMD.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -495,8 +501,297 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, (min_blocks<D, VARLEN>())) voi
   }
 }
 
+// d = 128 with an explicit ping-pong between two wave groups (FA3 explainer,
+// section "第二层重叠：Ping-Pong Scheduling"): eight waves per workgroup,
+// 32 query rows each; waves w and w + 4 share a SIMD.  The step of tile t is
+// split into a matrix part (S_t = K_t Q^T and O += V_{t-1}^T P_{t-1}^T) and a
+// vector part (mask, row max, rescale, exps and row sums of S_t).  In every
+// slot one group runs its matrix part while the other runs its vector part,
+// with a workgroup barrier between slots, so the two waves of a SIMD take
+// turns on the matrix core instead of contending for it.
+//   slot 2t:     group 0 matrix(t),  group 1 vector(t - 1)
+//   slot 2t + 1: group 0 vector(t),  group 1 matrix(t)
+// Stage t = {K_t, V_{t-1}} stays in LDS through slots 2t and 2t + 1.
+template <bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
+  constexpr int D = 128, BC = 64, NW = 8, QW = 32, BR = NW * QW;
+  constexpr int ROWB = D * 2, CPR = D / 8;
+  constexpr int INSTR = BC * ROWB / 1024;  // 1 KB wave-loads per tile
+  constexpr int IPW = INSTR / NW;
+  constexpr int RPI = 1024 / ROWB;
+  constexpr int NKB = BC / 32, NDB = D / 32, NQS = D / 16, NPS = BC / 16;
+
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks0[BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks1[BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs0[BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs1[BC * D];
+  __shared__ __attribute__((aligned(1024))) float Ost[4][QW * D];  // group 1's output staging
+
+  const int BH = p.B * p.H;
+  const int nq = (p.N + BR - 1) / BR;
+  int bh, qt;
+  if constexpr (CAUSAL) {
+    qt = nq - 1 - (int)blockIdx.x / BH;
+    bh = (int)blockIdx.x % BH;
+  } else {
+    const int w = xcd_contiguous((int)blockIdx.x, (int)gridDim.x);
+    bh = w / nq;
+    qt = w % nq;
+  }
+  const int bb = bh / p.H, hh = bh - bb * p.H;
+  const int hk = hh / (p.H / p.Hkv);
+  const int N = p.N, Nk = p.Nk;
+  const size_t qbase = (size_t)bh * N * D;
+  const size_t kvbase = ((size_t)bb * p.Hkv + hk) * Nk * D;
+  const size_t lbase = (size_t)bh * N;
+  const int off = Nk - N;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int grp = wave >> 2;
+  const int q0 = qt * BR + wave * QW;
+  const int qrow = q0 + l32;
+
+  // Q^T operands through range-checked buffer loads (rows past N read as
+  // zero): no branch around the loads, so the compiler can count them
+  bf16x8 qreg[NQS];
+  {
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(p.q + qbase, N * D * 2);
+#pragma unroll
+    for (int st = 0; st < NQS; ++st)
+      qreg[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, (qrow * D + (2 * st + hi) * 8) * 2, 0, 0));
+    // keep them ahead of the tile requests: the counter drains in order
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  const int kend = CAUSAL ? min(Nk, qt * BR + BR + off) : Nk;
+  const int T = kend > 0 ? (kend + BC - 1) / BC : 0;  // tiles of the workgroup
+  const int lastkey = q0 + QW - 1 + off;             // this wave's last visible key (causal)
+  const int Tw = CAUSAL ? (lastkey < 0 ? 0 : min(T, lastkey / BC + 1)) : T;  // tiles this wave uses
+
+  // the four waves of group 0 load each stage (8 KB each); group 1 loads nothing
+  const int kvrowb = D * 2;
+  const int kvbytes = Nk > 0 ? (Nk - 1) * kvrowb + ROWB : 0;
+  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(p.k + kvbase, kvbytes);
+  const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(p.v + kvbase, kvbytes);
+  constexpr int IPL = INSTR / 4;  // wave-loads per loading wave and tile
+  const int lw = wave & 3;
+  int koff[IPL], voff[IPL];
+#pragma unroll
+  for (int i = 0; i < IPL; ++i) {
+    const int row = (lw * IPL + i) * RPI + lane / CPR, pc = lane % CPR;
+    koff[i] = row * kvrowb + ((pc ^ k_swizzle<D>(row)) * 16);
+    voff[i] = row * kvrowb + ((pc ^ v_swizzle<D>(row)) * 16);
+  }
+  auto issue = [&](const __amdgpu_buffer_rsrc_t& r, uint16_t* dst, const int (&of)[IPL], int j) {
+#pragma unroll
+    for (int i = 0; i < IPL; ++i) lds_dma16(r, dst + (lw * IPL + i) * 512, of[i] + j * BC * kvrowb);
+  };
+
+  const int grpv = lane >> 4, sl = lane & 15;
+  const int v_row_in = sl >> 2;
+  const int v_col_in = 16 * (grpv & 1) + 4 * (sl & 3);
+  auto read_vt = [&](const uint16_t* vs, int kbase, int db) __attribute__((always_inline)) -> i16x4 {
+    const int row = kbase + v_row_in;
+    const int col = 32 * db + v_col_in;
+    const int e = row * D + (((col >> 3) ^ v_swizzle<D>(row)) << 3) + (col & 7);
+    return lds_read_tr16(&vs[e]);
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+  f32x16 sc[NKB];
+  bf16x8 pb[NPS];
+  const float c = p.c;
+  const float lazy = kLazyLog2 / c;
+
+  // matrix part of stage t: S_t = K_t Q^T, then O^T += V_{t-1}^T P_{t-1}^T
+  auto mfma_part = [&](int t, const uint16_t* kt, const uint16_t* vt) __attribute__((always_inline)) {
+    if (t < Tw) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) sc[kb] = f32x16{};
+#pragma unroll
+      for (int st = 0; st < NQS; ++st)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int row = kb * 32 + l32;
+          const bf16x8 a =
+              *reinterpret_cast<const bf16x8*>(&kt[row * D + (((2 * st + hi) ^ k_swizzle<D>(row)) * 8)]);
+          sc[kb] = mfma_bf16_32x32x16(a, qreg[st], sc[kb]);
+        }
+      // K operand reads three ahead of their products
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+      for (int i = 0; i < NQS * NKB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < NQS * NKB - 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    if (t >= 1 && t <= Tw) {
+#pragma unroll
+      for (int ks = 0; ks < NPS; ++ks)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const i16x4 a0 = read_vt(vt, 16 * ks + 4 * hi, db);
+          const i16x4 a1 = read_vt(vt, 16 * ks + 8 + 4 * hi, db);
+          const u32x2 w0 = __builtin_bit_cast(u32x2, a0), w1 = __builtin_bit_cast(u32x2, a1);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
+          o[db] = mfma_bf16_32x32x16(a, pb[ks], o[db]);
+        }
+      // transposed V reads two products ahead
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < NPS * NDB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < NPS * NDB - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+    }
+  };
+
+  // vector part of stage t: mask, row max, rescale, P_t = exp2 and row sums of S_t
+  auto vector_part = [&](int t) __attribute__((always_inline)) {
+    if (t >= Tw) return;
+    const int key0 = t * BC;
+    const bool need_mask = (CAUSAL && key0 + BC - 1 > q0 + off) || (key0 + BC > Nk);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const bool dead = (CAUSAL && key > qrow + off) || key >= Nk;
+          sc[kb][r] = dead ? -INFINITY : sc[kb][r];
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmax3(mx, sc[kb][r], sc[kb][r + 1]);
+    mx = max_halves(mx);
+    if (__any(mx > m_run + lazy)) {
+      const float m_new = __builtin_fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : exp2_fast((m_run - m_new) * c);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+      m_run = m_new;
+    }
+    const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NPS; ++ks) {
+      const int kb = ks >> 1, r0 = (ks & 1) * 8;
+      u32x4 w;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float e0 = exp2_fast(__builtin_fmaf(sc[kb][r0 + 2 * h], c, -mc));
+        const float e1 = exp2_fast(__builtin_fmaf(sc[kb][r0 + 2 * h + 1], c, -mc));
+        w[h] = pack_bf16x2(e0, e1);
+        ls[h] += e0 + e1;
+      }
+      pb[ks] = __builtin_bit_cast(bf16x8, w);
+    }
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
+
+  // Both groups run the same sequence, group 1 one slot later: stage t is
+  // [group 0 requests stage t + 1] matrix(t) | barrier | vector(t) [group 0
+  // waits for its requests] | barrier.  Group 0's matrix(t) falls in slot 2t
+  // and group 1's in slot 2t + 1; stage t + 1 lands before slot 2t + 2, and
+  // its ring slot last served stage t - 1, which group 1 finished in slot
+  // 2t - 1.
+  auto stage = [&](int t, const uint16_t* kt, const uint16_t* vt, uint16_t* k_fill, uint16_t* v_fill)
+                   __attribute__((always_inline)) {
+    if (grp == 0 && t >= 1) {  // stage 1 goes out with K_0 in the prologue
+      if (t + 1 < T) issue(rk, k_fill, koff, t + 1);
+      if (t < T) issue(rv, v_fill, voff, t);
+    }
+    mfma_part(t, kt, vt);
+    // phase switch only: no memory is handed over here (the stage being read
+    // landed at the previous end-of-stage barrier, the vector part touches no
+    // LDS, and every K/V read of the matrix part is consumed by its product
+    // before the wave gets here), so no fence and no wait for the requests
+    // just issued
+    __builtin_amdgcn_s_barrier();
+    vector_part(t);
+    wait_vmem_all();
+    __syncthreads();
+  };
+
+  // prologue: K_0, then stage 1 = {K_1, V_0}, requested whatever T is (past
+  // the keys the range check returns zeros; tiles past T land unused); wait
+  // for Q and K_0 only (the vector-memory counter drains in order)
+  if (grp == 0) {
+    issue(rk, Ks0, koff, 0);
+    issue(rk, Ks1, koff, 1);
+    issue(rv, Vs0, voff, 0);
+    static_assert(2 * IPL == 8, "the wait below counts the 8 requests of stage 1");
+    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8); expcnt, lgkmcnt left open
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), visible to the compiler's own wait tracking
+  }
+  // K_0 landed (each loading wave waited for its share); stage 1 may still be
+  // in flight, so a plain barrier (the fence of __syncthreads would drain it)
+  // that the compiler may not move LDS accesses across
+  asm volatile("s_barrier" ::: "memory");
+  if (grp == 1) __syncthreads();  // group 1 sits out slot 0
+  // stage t: K_t in slot t mod 2, V_{t-1} in slot (t - 1) mod 2; stage 0
+  // peeled, so the loop is entered after its drain at the end of stage 0
+  stage(0, Ks0, Vs1, Ks1, Vs0);
+  for (int t = 1; t <= T; t += 2) {
+    stage(t, Ks1, Vs0, Ks0, Vs1);
+    if (t + 1 <= T) stage(t + 1, Ks0, Vs1, Ks1, Vs0);
+  }
+  if (grp == 0) __syncthreads();  // group 0 sits out the last slot
+
+  // epilogue: O / l staged through LDS (group 0 in the ring, group 1 in its
+  // own 64 KB) and stored as whole rows; every wave is past its last ring
+  // read (the final barrier above)
+  const float l_tot = sum_halves(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qrow < N && hi == 0) p.lse[lbase + qrow] = m_run * p.scale + __logf(l_tot);
+  constexpr int CPO = D / 4;  // 16-byte chunks per fp32 row
+  float* st = wave >= 4 ? Ost[wave - 4]
+                        : reinterpret_cast<float*>(wave == 0 ? Ks0 : wave == 1 ? Ks1 : wave == 2 ? Vs0 : Vs1);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int cc = 8 * db + 2 * g + hi;  // chunk of d = 32 db + 8 g + 4 hi .. +3
+      const f32x4 val = {o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv};
+      *reinterpret_cast<f32x4*>(st + l32 * D + ((cc ^ (l32 & (CPO - 1))) * 4)) = val;
+    }
+  constexpr int RPS = 64 / CPO;  // rows per store instruction
+#pragma unroll
+  for (int t = 0; t < 32 / RPS; ++t) {
+    const int r = t * RPS + lane / CPO, cc = lane % CPO;
+    const f32x4 val = *reinterpret_cast<const f32x4*>(st + r * D + ((cc ^ (r & (CPO - 1))) * 4));
+    if (q0 + r < N) *reinterpret_cast<f32x4*>(p.o + qbase + (size_t)(q0 + r) * D + 4 * cc) = val;
+  }
+}
+
+// The ping-pong kernel takes d = 128 fixed-length batches with at least 1024
+// query rows (512 non-causal); shorter ones keep 128-row workgroups, which
+// balance short causal grids better and leave fewer idle rows (same-box
+// measurements: ping-pong 1.03-1.10 x from N = 1024 up, 0.97 x at N = 512
+// causal).
+inline bool use_pingpong(const FwdBf16Params& p, bool causal) { return p.N >= 1024 || (!causal && p.N >= 512); }
+
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch(const FwdBf16Params& p, hipStream_t stream) {
+  if constexpr (D == 128 && !VARLEN) {
+    if (use_pingpong(p, CAUSAL)) {
+      const int nq = (p.N + 255) / 256;
+      const unsigned grid = (unsigned)nq * (unsigned)p.B * (unsigned)p.H;
+      if (grid == 0) return hipSuccess;
+      hipLaunchKernelGGL((fwd_bf16_pp_kernel<CAUSAL>), dim3(grid), dim3(512), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
   constexpr int BR = rows_per_workgroup<D>();
   const int nq = (p.N + BR - 1) / BR;
   const unsigned grid = (unsigned)nq * (unsigned)p.B * (unsigned)p.H;
