@@ -512,6 +512,12 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, (min_blocks<D, VARLEN>())) voi
 //   slot 2t:     group 0 matrix(t),  group 1 vector(t - 1)
 //   slot 2t + 1: group 0 vector(t),  group 1 matrix(t)
 // Stage t = {K_t, V_{t-1}} stays in LDS through slots 2t and 2t + 1.
+#ifndef FA_PP_KLEAD
+#define FA_PP_KLEAD 3
+#endif
+#ifndef FA_PP_VLEAD
+#define FA_PP_VLEAD 4
+#endif
 template <bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
   constexpr int D = 128, BC = 64, NW = 8, QW = 32, BR = NW * QW;
@@ -609,45 +615,56 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
   const float lazy = kLazyLog2 / c;
 
   // matrix part of stage t: S_t = K_t Q^T, then O^T += V_{t-1}^T P_{t-1}^T
+  auto qk_part = [&](const uint16_t* kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sc[kb] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < NQS; ++st)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int row = kb * 32 + l32;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kt[row * D + (((2 * st + hi) ^ k_swizzle<D>(row)) * 8)]);
+        sc[kb] = mfma_bf16_32x32x16(a, qreg[st], sc[kb]);
+      }
+  };
+  auto pv_part = [&](const uint16_t* vt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < NPS; ++ks)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const i16x4 a0 = read_vt(vt, 16 * ks + 4 * hi, db);
+        const i16x4 a1 = read_vt(vt, 16 * ks + 8 + 4 * hi, db);
+        const u32x2 w0 = __builtin_bit_cast(u32x2, a0), w1 = __builtin_bit_cast(u32x2, a1);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
+        o[db] = mfma_bf16_32x32x16(a, pb[ks], o[db]);
+      }
+  };
+  // K operand reads FA_PP_KLEAD ahead of their products
+  auto sched_qk = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_group_barrier(0x100, FA_PP_KLEAD, 0);
+#pragma unroll
+    for (int i = 0; i < NQS * NKB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < NQS * NKB - FA_PP_KLEAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  // transposed V reads FA_PP_VLEAD ahead (two per product)
+  auto sched_pv = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_group_barrier(0x100, FA_PP_VLEAD, 0);
+#pragma unroll
+    for (int i = 0; i < NPS * NDB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < NPS * NDB - FA_PP_VLEAD / 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  };
   auto mfma_part = [&](int t, const uint16_t* kt, const uint16_t* vt) __attribute__((always_inline)) {
     if (t < Tw) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) sc[kb] = f32x16{};
-#pragma unroll
-      for (int st = 0; st < NQS; ++st)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const int row = kb * 32 + l32;
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(&kt[row * D + (((2 * st + hi) ^ k_swizzle<D>(row)) * 8)]);
-          sc[kb] = mfma_bf16_32x32x16(a, qreg[st], sc[kb]);
-        }
-      // K operand reads three ahead of their products
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-#pragma unroll
-      for (int i = 0; i < NQS * NKB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i < NQS * NKB - 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
+      qk_part(kt);
+      sched_qk();
     }
     if (t >= 1 && t <= Tw) {
-#pragma unroll
-      for (int ks = 0; ks < NPS; ++ks)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const i16x4 a0 = read_vt(vt, 16 * ks + 4 * hi, db);
-          const i16x4 a1 = read_vt(vt, 16 * ks + 8 + 4 * hi, db);
-          const u32x2 w0 = __builtin_bit_cast(u32x2, a0), w1 = __builtin_bit_cast(u32x2, a1);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
-          o[db] = mfma_bf16_32x32x16(a, pb[ks], o[db]);
-        }
-      // transposed V reads two products ahead
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int i = 0; i < NPS * NDB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i < NPS * NDB - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
+      pv_part(vt);
+      sched_pv();
     }
   };
 
