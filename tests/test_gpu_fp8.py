@@ -128,7 +128,7 @@ def _fp8_pipeline(q, k, v, signs, mode, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("N", [64, 128, 200, 777, 1024])
+@pytest.mark.parametrize("N", [64, 128, 200, 777, 1024, 1100, 1537, 2100, 4100])
 def test_fwd_fp8_matches_emulation_of_its_operands(gpu_lib, N, causal):
     B, H, d = 1, 2, 128
     q, k, v = make_qkv(B, H, N, d, seed=5000 + N, outliers=True)
