@@ -515,12 +515,13 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, (min_blocks<D, VARLEN>())) voi
 #ifndef FA_PP_KLEAD
 #define FA_PP_KLEAD 3
 #endif
+
 #ifndef FA_PP_VLEAD
 #define FA_PP_VLEAD 4
 #endif
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
-  constexpr int D = 128, BC = 64, NW = 8, QW = 32, BR = NW * QW;
+  constexpr int BC = D == 256 ? 32 : 64, NW = 8, QW = 32, BR = NW * QW;
   constexpr int ROWB = D * 2, CPR = D / 8;
   constexpr int INSTR = BC * ROWB / 1024;  // 1 KB wave-loads per tile
   constexpr int IPW = INSTR / NW;
@@ -531,7 +532,9 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
   __shared__ __attribute__((aligned(1024))) uint16_t Ks1[BC * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Vs0[BC * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Vs1[BC * D];
-  __shared__ __attribute__((aligned(1024))) float Ost[4][QW * D];  // group 1's output staging
+  // O is staged through LDS where a wave's fp32 tile fits a ring slot (d = 64, 128)
+  constexpr bool kStageO = QW * D * 4 <= BC * D * 2;
+  __shared__ __attribute__((aligned(1024))) float Ost[4][kStageO ? QW * D : 1];  // group 1's output staging
 
   const int BH = p.B * p.H;
   const int nq = (p.N + BR - 1) / BR;
@@ -639,22 +642,23 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
         o[db] = mfma_bf16_32x32x16(a, pb[ks], o[db]);
       }
   };
-  // K operand reads FA_PP_KLEAD ahead of their products
+  // K operand reads KL ahead of their products, transposed V reads VL ahead
+  // (two per product); at d = 256 shorter leads keep the wave within 256 VGPRs
+  constexpr int KL = D == 256 ? 1 : FA_PP_KLEAD, VL = D == 256 ? 2 : FA_PP_VLEAD;
   auto sched_qk = [&]() __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_group_barrier(0x100, FA_PP_KLEAD, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, KL, 0);
 #pragma unroll
     for (int i = 0; i < NQS * NKB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < NQS * NKB - FA_PP_KLEAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < NQS * NKB - KL) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
-  // transposed V reads FA_PP_VLEAD ahead (two per product)
   auto sched_pv = [&]() __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_group_barrier(0x100, FA_PP_VLEAD, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, VL, 0);
 #pragma unroll
     for (int i = 0; i < NPS * NDB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < NPS * NDB - FA_PP_VLEAD / 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (i < NPS * NDB - VL / 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
   auto mfma_part = [&](int t, const uint16_t* kt, const uint16_t* vt) __attribute__((always_inline)) {
@@ -746,8 +750,8 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
     issue(rk, Ks0, koff, 0);
     issue(rk, Ks1, koff, 1);
     issue(rv, Vs0, voff, 0);
-    static_assert(2 * IPL == 8, "the wait below counts the 8 requests of stage 1");
-    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8); expcnt, lgkmcnt left open
+    static_assert(2 * IPL <= 15, "the wait below encodes vmcnt in 4 bits");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * IPL));  // vmcnt(stage 1's requests); expcnt, lgkmcnt left open
   } else {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), visible to the compiler's own wait tracking
   }
@@ -765,29 +769,40 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
   }
   if (grp == 0) __syncthreads();  // group 0 sits out the last slot
 
-  // epilogue: O / l staged through LDS (group 0 in the ring, group 1 in its
-  // own 64 KB) and stored as whole rows; every wave is past its last ring
-  // read (the final barrier above)
+  // epilogue: O / l, staged through LDS where it fits (group 0 in the ring,
+  // group 1 in its own area) and stored as whole rows; every wave is past its
+  // last ring read (the final barrier above)
   const float l_tot = sum_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < N && hi == 0) p.lse[lbase + qrow] = m_run * p.scale + __logf(l_tot);
-  constexpr int CPO = D / 4;  // 16-byte chunks per fp32 row
-  float* st = wave >= 4 ? Ost[wave - 4]
-                        : reinterpret_cast<float*>(wave == 0 ? Ks0 : wave == 1 ? Ks1 : wave == 2 ? Vs0 : Vs1);
+  if constexpr (kStageO) {
+    constexpr int CPO = D / 4;  // 16-byte chunks per fp32 row
+    float* st = wave >= 4 ? Ost[wave - 4]
+                          : reinterpret_cast<float*>(wave == 0 ? Ks0 : wave == 1 ? Ks1 : wave == 2 ? Vs0 : Vs1);
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int cc = 8 * db + 2 * g + hi;  // chunk of d = 32 db + 8 g + 4 hi .. +3
-      const f32x4 val = {o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv};
-      *reinterpret_cast<f32x4*>(st + l32 * D + ((cc ^ (l32 & (CPO - 1))) * 4)) = val;
+      for (int g = 0; g < 4; ++g) {
+        const int cc = 8 * db + 2 * g + hi;  // chunk of d = 32 db + 8 g + 4 hi .. +3
+        const f32x4 val = {o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv};
+        *reinterpret_cast<f32x4*>(st + l32 * D + ((cc ^ (l32 & (CPO - 1))) * 4)) = val;
+      }
+    constexpr int RPS = 64 / CPO;  // rows per store instruction
+#pragma unroll
+    for (int t = 0; t < 32 / RPS; ++t) {
+      const int r = t * RPS + lane / CPO, cc = lane % CPO;
+      const f32x4 val = *reinterpret_cast<const f32x4*>(st + r * D + ((cc ^ (r & (CPO - 1))) * 4));
+      if (q0 + r < N) *reinterpret_cast<f32x4*>(p.o + qbase + (size_t)(q0 + r) * D + 4 * cc) = val;
     }
-  constexpr int RPS = 64 / CPO;  // rows per store instruction
+  } else if (qrow < N) {
+    float* orow = p.o + qbase + (size_t)qrow * D;
 #pragma unroll
-  for (int t = 0; t < 32 / RPS; ++t) {
-    const int r = t * RPS + lane / CPO, cc = lane % CPO;
-    const f32x4 val = *reinterpret_cast<const f32x4*>(st + r * D + ((cc ^ (r & (CPO - 1))) * 4));
-    if (q0 + r < N) *reinterpret_cast<f32x4*>(p.o + qbase + (size_t)(q0 + r) * D + 4 * cc) = val;
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 val = {o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv};
+        *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * g + 4 * hi) = val;
+      }
   }
 }
 
@@ -796,6 +811,10 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
 // balance short causal grids better and leave fewer idle rows (same-box
 // measurements: ping-pong 1.03-1.10 x from N = 1024 up, 0.97 x at N = 512
 // causal).
+// The kernel is written for d = 64 and 256 too (32-key stages at 256) but
+// only d = 128 is dispatched: measured on one box, d = 64 ran 0.97-1.05 x its
+// three-workgroups-per-CU kernel, and d = 256 needs more than 256 VGPRs (O
+// 128, Q 64) and spills 12-13 in the loop (0.62-0.79 x).
 inline bool use_pingpong(const FwdBf16Params& p, bool causal) { return p.N >= 1024 || (!causal && p.N >= 512); }
 
 template <int D, bool CAUSAL, bool VARLEN>
@@ -805,7 +824,7 @@ hipError_t launch(const FwdBf16Params& p, hipStream_t stream) {
       const int nq = (p.N + 255) / 256;
       const unsigned grid = (unsigned)nq * (unsigned)p.B * (unsigned)p.H;
       if (grid == 0) return hipSuccess;
-      hipLaunchKernelGGL((fwd_bf16_pp_kernel<CAUSAL>), dim3(grid), dim3(512), 0, stream, p);
+      hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, CAUSAL>), dim3(grid), dim3(512), 0, stream, p);
       return hipGetLastError();
     }
   }

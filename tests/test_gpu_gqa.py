@@ -62,13 +62,16 @@ def test_gqa_invalid_arguments():
 # d = 128 batches with at least 1024 query rows (512 non-causal) run on the
 # eight-wave ping-pong kernel: ragged lengths around its 256-row workgroups
 # and 64-key stages, grouped heads, bottom-right causal alignment both ways
-# (Nq > Nk leaves the first Nq - Nk rows without keys)
+# (Nq > Nk leaves the first Nq - Nk rows without keys); d = 64 and 256 cover
+# the same shapes on the four-wave kernel
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("Nq,Nk", [(1024, 1024), (1100, 1100), (1537, 1537), (1100, 1300), (1300, 1100),
                                    (1030, 70)])
-def test_pingpong_shapes(Nq, Nk, causal):
-    _check(1, 4, 2, Nq, Nk, 128, causal, seed=7300 + Nq + Nk)
+def test_pingpong_shapes(Nq, Nk, d, causal):
+    _check(1, 4, 2, Nq, Nk, d, causal, seed=7300 + Nq + Nk + d)
 
 
-def test_pingpong_noncausal_short():
-    _check(2, 2, 2, 600, 600, 128, False, seed=7400)
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_pingpong_noncausal_short(d):
+    _check(2, 2, 2, 600, 600, d, False, seed=7400 + d)
