@@ -51,8 +51,8 @@
 // cross a wave's diagonal are masked element-wise, waves whose rows all lie
 // above a tile skip its products, and the heaviest query tiles launch first.
 //
-// d = 128 batches of 1024 or more query rows run a second kernel,
-// fwd_bf16_pp_kernel (below): eight waves per workgroup in two groups that
+// d = 128 batches of 1024 or more query rows (fixed-length, or packed with
+// such a longest sequence) run a second kernel, fwd_bf16_pp_kernel (below): eight waves per workgroup in two groups that
 // take turns on each SIMD's matrix core (one group's products while the
 // other group's softmax), the FA3 explainer's ping-pong scheduling mapped to
 // wave pairs of a SIMD.
@@ -169,6 +169,41 @@ __device__ __forceinline__ void schedule_step() {
   }
 }
 
+// Where one (sequence, head) lives.  Fixed-length batch: [B, H, N, d] and
+// [B, Hkv, Nk, d], rows d apart.  Packed batch: sequence bb's rows of the
+// token-major tensors, H d (q, o) and Hkv d (k, v) apart, bounds clamped into
+// the tensors.
+template <bool VARLEN> struct SeqExtent {
+  int N, Nk;              // query and key rows
+  size_t qbase, kvbase;   // element offsets of row 0 of this (sequence, head)
+  int qstride, kvstride;  // elements between consecutive rows
+  size_t lbase;           // lse index of row 0
+};
+template <int D, bool VARLEN>
+__device__ __forceinline__ SeqExtent<VARLEN> seq_extent(const FwdBf16Params& p, int bb, int hh, int hk) {
+  SeqExtent<VARLEN> e;
+  if constexpr (VARLEN) {
+    const int q0s = min(max(p.cu_q[bb], 0), p.total_q), q1s = min(max(p.cu_q[bb + 1], q0s), p.total_q);
+    const int k0s = min(max(p.cu_k[bb], 0), p.total_k), k1s = min(max(p.cu_k[bb + 1], k0s), p.total_k);
+    e.N = q1s - q0s;
+    e.Nk = k1s - k0s;
+    e.qstride = p.H * D;
+    e.kvstride = p.Hkv * D;
+    e.qbase = (size_t)q0s * e.qstride + (size_t)hh * D;
+    e.kvbase = (size_t)k0s * e.kvstride + (size_t)hk * D;
+    e.lbase = (size_t)hh * p.total_q + q0s;
+  } else {
+    e.N = p.N;
+    e.Nk = p.Nk;
+    e.qstride = D;
+    e.kvstride = D;
+    e.qbase = ((size_t)bb * p.H + hh) * e.N * D;
+    e.kvbase = ((size_t)bb * p.Hkv + hk) * e.Nk * D;
+    e.lbase = ((size_t)bb * p.H + hh) * e.N;
+  }
+  return e;
+}
+
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, (min_blocks<D, VARLEN>())) void fwd_bf16_kernel(FwdBf16Params p) {
   using Cfg = Bf16Cfg<D>;
@@ -210,33 +245,10 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, (min_blocks<D, VARLEN>())) voi
   const int bb = bh / p.H, hh = bh - bb * p.H;
   const int hk = hh / (p.H / p.Hkv);
 
-  // Per-sequence extents.  Fixed-length batch: [B, H, N, d] and [B, Hkv, Nk, d],
-  // rows d apart.  Packed batch: sequence bb's rows of the token-major tensors,
-  // H d (q, o) and Hkv d (k, v) apart, bounds clamped into the tensors.
-  int N, Nk;
-  size_t qbase, kvbase;  // element offsets of row 0 of this (sequence, head)
-  int qstride, kvstride;  // elements between consecutive rows
-  size_t lbase;           // lse index of row 0
-  if constexpr (VARLEN) {
-    const int q0s = min(max(p.cu_q[bb], 0), p.total_q), q1s = min(max(p.cu_q[bb + 1], q0s), p.total_q);
-    const int k0s = min(max(p.cu_k[bb], 0), p.total_k), k1s = min(max(p.cu_k[bb + 1], k0s), p.total_k);
-    N = q1s - q0s;
-    Nk = k1s - k0s;
-    if (qt * BR >= N) return;  // past this sequence's queries: the whole workgroup leaves
-    qstride = p.H * D;
-    kvstride = p.Hkv * D;
-    qbase = (size_t)q0s * qstride + (size_t)hh * D;
-    kvbase = (size_t)k0s * kvstride + (size_t)hk * D;
-    lbase = (size_t)hh * p.total_q + q0s;
-  } else {
-    N = p.N;
-    Nk = p.Nk;
-    qstride = D;
-    kvstride = D;
-    qbase = (size_t)bh * N * D;
-    kvbase = ((size_t)bb * p.Hkv + hk) * Nk * D;
-    lbase = (size_t)bh * N;
-  }
+  const SeqExtent<VARLEN> ex = seq_extent<D, VARLEN>(p, bb, hh, hk);
+  const int N = ex.N, Nk = ex.Nk, qstride = ex.qstride, kvstride = ex.kvstride;
+  const size_t qbase = ex.qbase, kvbase = ex.kvbase, lbase = ex.lbase;
+  if (VARLEN && qt * BR >= N) return;  // past this sequence's queries: the whole workgroup leaves
   const int off = Nk - N;  // causal alignment: query i sees keys j <= i + off
 
   const int tid = threadIdx.x;
@@ -519,7 +531,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, (min_blocks<D, VARLEN>())) voi
 #ifndef FA_PP_VLEAD
 #define FA_PP_VLEAD 4
 #endif
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
   constexpr int BC = D == 256 ? 32 : 64, NW = 8, QW = 32, BR = NW * QW;
   constexpr int ROWB = D * 2, CPR = D / 8;
@@ -549,10 +561,10 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
   }
   const int bb = bh / p.H, hh = bh - bb * p.H;
   const int hk = hh / (p.H / p.Hkv);
-  const int N = p.N, Nk = p.Nk;
-  const size_t qbase = (size_t)bh * N * D;
-  const size_t kvbase = ((size_t)bb * p.Hkv + hk) * Nk * D;
-  const size_t lbase = (size_t)bh * N;
+  const SeqExtent<VARLEN> ex = seq_extent<D, VARLEN>(p, bb, hh, hk);
+  const int N = ex.N, Nk = ex.Nk, qstride = ex.qstride;
+  const size_t qbase = ex.qbase, kvbase = ex.kvbase, lbase = ex.lbase;
+  if (VARLEN && qt * BR >= N) return;  // past this sequence's queries: the whole workgroup leaves
   const int off = Nk - N;
 
   const int tid = threadIdx.x;
@@ -566,10 +578,10 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
   // zero): no branch around the loads, so the compiler can count them
   bf16x8 qreg[NQS];
   {
-    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(p.q + qbase, N * D * 2);
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(p.q + qbase, N > 0 ? ((N - 1) * qstride + D) * 2 : 0);
 #pragma unroll
     for (int st = 0; st < NQS; ++st)
-      qreg[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, (qrow * D + (2 * st + hi) * 8) * 2, 0, 0));
+      qreg[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, (qrow * qstride + (2 * st + hi) * 8) * 2, 0, 0));
     // keep them ahead of the tile requests: the counter drains in order
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -580,7 +592,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
   const int Tw = CAUSAL ? (lastkey < 0 ? 0 : min(T, lastkey / BC + 1)) : T;  // tiles this wave uses
 
   // the four waves of group 0 load each stage (8 KB each); group 1 loads nothing
-  const int kvrowb = D * 2;
+  const int kvrowb = ex.kvstride * 2;
   const int kvbytes = Nk > 0 ? (Nk - 1) * kvrowb + ROWB : 0;
   const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(p.k + kvbase, kvbytes);
   const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(p.v + kvbase, kvbytes);
@@ -792,10 +804,10 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
     for (int t = 0; t < 32 / RPS; ++t) {
       const int r = t * RPS + lane / CPO, cc = lane % CPO;
       const f32x4 val = *reinterpret_cast<const f32x4*>(st + r * D + ((cc ^ (r & (CPO - 1))) * 4));
-      if (q0 + r < N) *reinterpret_cast<f32x4*>(p.o + qbase + (size_t)(q0 + r) * D + 4 * cc) = val;
+      if (q0 + r < N) *reinterpret_cast<f32x4*>(p.o + qbase + (size_t)(q0 + r) * qstride + 4 * cc) = val;
     }
   } else if (qrow < N) {
-    float* orow = p.o + qbase + (size_t)qrow * D;
+    float* orow = p.o + qbase + (size_t)qrow * qstride;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -806,11 +818,11 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
   }
 }
 
-// The ping-pong kernel takes d = 128 fixed-length batches with at least 1024
-// query rows (512 non-causal); shorter ones keep 128-row workgroups, which
-// balance short causal grids better and leave fewer idle rows (same-box
-// measurements: ping-pong 1.03-1.10 x from N = 1024 up, 0.97 x at N = 512
-// causal).
+// The ping-pong kernel takes d = 128 batches whose longest sequence has at
+// least 1024 query rows (512 non-causal), fixed-length or packed; shorter ones
+// keep 128-row workgroups, which balance short causal grids better and leave
+// fewer idle rows (same-box measurements: ping-pong 1.03-1.10 x from N = 1024
+// up, 0.97 x at N = 512 causal; packed batches of 128-8192 rows 1.05-1.12 x).
 // The kernel is written for d = 64 and 256 too (32-key stages at 256) but
 // only d = 128 is dispatched: measured on one box, d = 64 ran 0.97-1.05 x its
 // three-workgroups-per-CU kernel, and d = 256 needs more than 256 VGPRs (O
@@ -819,12 +831,12 @@ inline bool use_pingpong(const FwdBf16Params& p, bool causal) { return p.N >= 10
 
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch(const FwdBf16Params& p, hipStream_t stream) {
-  if constexpr (D == 128 && !VARLEN) {
+  if constexpr (D == 128) {
     if (use_pingpong(p, CAUSAL)) {
       const int nq = (p.N + 255) / 256;
       const unsigned grid = (unsigned)nq * (unsigned)p.B * (unsigned)p.H;
       if (grid == 0) return hipSuccess;
-      hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, CAUSAL>), dim3(grid), dim3(512), 0, stream, p);
+      hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, CAUSAL, VARLEN>), dim3(grid), dim3(512), 0, stream, p);
       return hipGetLastError();
     }
   }

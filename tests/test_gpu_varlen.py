@@ -58,16 +58,33 @@ def test_varlen_cross_lengths_and_sequences_without_keys(causal):
     _run([1, 3, 20, 17], [100, 0, 5, 400], 6, 1, 128, causal, seed=7720)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_pingpong_lengths(causal):
+    # longest sequence >= 1024 rows at d = 128: 256-row workgroups of eight
+    # waves; lengths straddle their edges, keys longer and shorter than queries
+    lq = [1100, 0, 1, 255, 257, 2049, 700]
+    lk = [1100, 0, 1, 255, 300, 2049, 650]
+    _run(lq, lk, 4, 2, 128, causal, seed=7750)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_pingpong_sequences_without_keys(causal):
+    # rows past every key of their sequence, a sequence with no keys at all
+    _run([1030, 3, 600, 513], [70, 0, 1500, 513], 3, 1, 128, causal, seed=7760)
+
+
 def test_varlen_grid_larger_than_needed():
     _run([50, 70], [50, 70], 2, 1, 128, True, seed=7730, max_q=1000)
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_varlen_equal_lengths_match_fixed_length_forward(causal):
-    # three sequences of 300: the same per-tile work as the [B, H, N, d] call, bit for bit
-    B, Hq, Hkv, N, d = 3, 4, 2, 300, 128
-    q, _, _ = make_qkv(B, Hq, N, d, 7740)
-    _, k, v = make_qkv(B, Hkv, N, d, 7741)
+@pytest.mark.parametrize("N", [300, 1100])
+def test_varlen_equal_lengths_match_fixed_length_forward(N, causal):
+    # three sequences of N: the same per-tile work as the [B, H, N, d] call, bit
+    # for bit (N = 1100: both take the 256-row ping-pong workgroups)
+    B, Hq, Hkv, d = 3, 4, 2, 128
+    q, _, _ = make_qkv(B, Hq, N, d, 7740 + N)
+    _, k, v = make_qkv(B, Hkv, N, d, 7741 + N)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     o4, l4 = fa.fwd_bf16_gqa(qd, kd, vd, causal=causal)
     pack = lambda x: x.transpose(1, 2).reshape(B * N, x.shape[1], d).contiguous()
