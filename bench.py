@@ -171,7 +171,8 @@ def main():
     import torch
 
     import exact_attention_73_amd as fa
-    from exact_attention_73_amd.inputs import WORKLOADS, make_do, make_qkv, make_signs, softmax_scale, sweep_workloads
+    from exact_attention_73_amd.inputs import (WORKLOADS, make_do, make_qkv, make_signs, packed_batch_lengths,
+                                              softmax_scale, sweep_workloads)
 
     fa.load()
     dev = torch.device("cuda:0")
@@ -370,8 +371,7 @@ def main():
         # 16 causal sequences of mixed lengths (seeded, 256..4096 keys) packed
         # end to end; FLOPs count each sequence's own work only.  The same
         # batch padded to its longest sequence is timed beside it.
-        g = torch.Generator("cpu").manual_seed(73800)
-        lens = [int(x) for x in torch.randint(256, 4097, (16,), generator=g)]
+        lens = packed_batch_lengths()
         Hv, dv_ = 16, 128
         tot = sum(lens)
         qv_, _, _ = make_qkv(1, Hv, tot, dv_, 73801)

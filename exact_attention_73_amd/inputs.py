@@ -82,6 +82,15 @@ WORKLOADS = {
 }
 
 
+def packed_batch_lengths(n_seq: int = 16, lo: int = 256, hi: int = 4096, seed: int = 73800) -> list:
+    """Sequence lengths of the packed variable-length workload: n_seq seeded
+    draws, uniform on [lo, hi] (16 sequences, 36194 tokens by default);
+    q is make_qkv(1, H, total, d, seed + 1), k and v make_qkv(..., seed + 2),
+    each moved to the token-major [total, H, d] layout."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    return [int(x) for x in torch.randint(lo, hi + 1, (n_seq,), generator=g)]
+
+
 def sweep_workloads():
     """Sequence-length sweep at 16384 total tokens and hidden size 2048."""
     out = []

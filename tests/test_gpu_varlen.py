@@ -9,9 +9,9 @@ import pytest
 import torch
 
 import exact_attention_73_amd as fa
-from exact_attention_73_amd.inputs import make_qkv, softmax_scale
-from oracle import attention_varlen_ref
-from tests._util import check_rows
+from exact_attention_73_amd.inputs import make_qkv, packed_batch_lengths, softmax_scale
+from oracle import attention_ref, attention_varlen_ref
+from tests._util import check_rows, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -93,3 +93,30 @@ def test_varlen_equal_lengths_match_fixed_length_forward(N, causal):
     torch.cuda.synchronize()
     assert torch.equal(o, o4.transpose(1, 2).reshape(B * N, Hq, d))
     assert torch.equal(lse, l4.permute(1, 0, 2).reshape(Hq, B * N))
+
+
+def test_varlen_packed_workload_sampled():
+    """The packed batch bench.py times (16 causal sequences of 256..4096
+    tokens, 36194 in all, H16 d128, the ping-pong kernel), in the same launch:
+    sampled rows of every sequence, on three heads, against the oracle run
+    on each sequence alone."""
+    lens = packed_batch_lengths()
+    H, d = 16, 128
+    tot = sum(lens)
+    q, _, _ = make_qkv(1, H, tot, d, 73801)
+    _, k, v = make_qkv(1, H, tot, d, 73802)
+    q, k, v = (x[0].transpose(0, 1).contiguous() for x in (q, k, v))  # [total, H, d]
+    cu = np.cumsum([0] + lens)
+    cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    o, lse = fa.fwd_bf16_varlen(q.cuda(), k.cuda(), v.cuda(), cu_d, cu_d, max(lens), causal=True)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    sc = softmax_scale(d)
+    for s_, n in enumerate(lens):
+        a = int(cu[s_])
+        rows = sample_rows(n, extra=8, seed=s_)
+        for h in (0, 7, H - 1):
+            seq = lambda x: x[a:a + n, h][None, None]  # [1, 1, n, d]
+            o_ref, lse_ref = attention_ref(seq(q), seq(k), seq(v), causal=True, scale=sc, rows=rows)
+            check_rows(o[a + rows, h][None, None], lse[h, a + rows][None, None], o_ref, lse_ref,
+                       f"packed workload seq {s_} (n={n}) head {h}")
