@@ -571,7 +571,10 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int grp = wave >> 2;
-  const int q0 = qt * BR + wave * QW;
+  // causal: group 0, which runs one slot ahead, takes the later 128 rows
+  // (the ones with the most key tiles), so the workgroup ends with group 0's
+  // last vector part rather than one slot after it
+  const int q0 = qt * BR + (CAUSAL ? (wave ^ 4) : wave) * QW;
   const int qrow = q0 + l32;
 
   // Q^T operands through range-checked buffer loads (rows past N read as
