@@ -14,15 +14,17 @@ What the pages fix, and the readings taken where they are silent:
   (batch, head), all of d (P1 section "Block Quantization 为什么优于
   Per-Tensor Scale" keeps one scale per B_r x d or B_c x d tile; the block
   height of 128 is the plain choice for tiles of 128 query rows).  The scale
-  formula was lost from the page text; s = amax / 448 for Q and K, and s = 1
-  for an all-zero block.  For V, the operand of the PV product, s is the
-  power of two 2^ceil(log2(amax / 448)): the matrix instruction's E8M0
-  block exponent then carries it exactly, its codes are exact in any
-  precision, and the largest probability (P = 1) maps to a representable
-  value instead of landing on an E4M3 rounding tie (with s = amax / 448 and
-  bf16 amax, 2^7 * mantissa(s) often is a tie, e.g. 232 between 224 and
-  240).  Per-tensor mode uses one amax over the whole tensor (the same
-  section's baseline, one scale for all of Q).
+  formula was lost from the page text; the plain reading with the 448 bound
+  of P2 section 三.3 is s = amax / 448 for each of Q, K and V, and s = 1 for
+  an all-zero block.  The code of an entry is the E4M3 rounding of the exact
+  quotient y / s (float64 here; no page fixes a precision), so a kernel that
+  forms the quotient in fp32 may land one code step away where the exact
+  quotient sits within fp32 rounding of a tie.  A power-of-two V scale,
+  2^ceil(log2(amax / 448)), is kept as a variant (``pow2``): the matrix
+  instruction's E8M0 block exponent carries it exactly and its codes are
+  exact in any precision, at the cost of up to one bit of V's range.
+  Per-tensor mode uses one amax over the whole tensor (the same section's
+  baseline, one scale for all of Q).
 * Incoherent processing: Q and K are both multiplied by the same random
   orthogonal matrix M = diag(sigma) H_d / sqrt(d), sigma a per-head vector of
   +-1 and H_d the Sylvester Hadamard matrix (P1 section "Incoherent
@@ -163,13 +165,12 @@ def quantize_fp8(x, signs=None, per_tensor: bool = False, block: int = SCALE_BLO
     With u = x diag(sigma) H_d (unnormalised; u = x without rotation) and
     r = sqrt(d) (1 without rotation), the rotated tensor is y = u / r, the
     block amax is a = max |u| / r and the scale s = a / 448.  The code is
-    RNE(y / s) = RNE(u * 448 / max|u|); that value decides an integer, so it
-    is taken in float32 exactly as the kernel forms it (the pages fix no
-    precision): code = E4M3(clamp(fl32(fl32(u) * fl32(448 / fl32(max|u|))))).
+    the E4M3 rounding (nearest, ties to even) of y / s = u * 448 / max|u|,
+    taken in float64: u * 448 is exact there and the division rounds once.
 
-    With ``pow2`` (the PV operand V; no rotation) the scale is the power of
-    two s = 2^ceil(log2(a / 448)), the smallest one with a / s <= 448, and the
-    code RNE(y / s) is exact in any precision.
+    With ``pow2`` (a variant for the PV operand V; no rotation) the scale is
+    the power of two s = 2^ceil(log2(a / 448)), the smallest one with
+    a / s <= 448, and the code RNE(y / s) is exact in any precision.
 
     Returns ``(codes, scale, y)``:
       codes uint8 ``[B, H, N, d]`` (None when ``quantize`` is False),
@@ -200,11 +201,10 @@ def quantize_fp8(x, signs=None, per_tensor: bool = False, block: int = SCALE_BLO
     scale = np.where(amax > 0, amax / (E4M3_MAX * r), 1.0)
     if not quantize:
         return None, scale, y
-    a32 = np.repeat(amax, block, axis=2)[:, :, :N, None].astype(np.float32)
-    with np.errstate(divide="ignore"):
-        inv32 = np.where(a32 > 0, np.float32(E4M3_MAX) / a32, np.float32(0)).astype(np.float32)
-    q32 = (u.astype(np.float32) * inv32).astype(np.float32)
-    codes = e4m3_encode(np.clip(q32.astype(np.float64), -E4M3_MAX, E4M3_MAX))
+    a_rows = np.repeat(amax, block, axis=2)[:, :, :N, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        quot = np.where(a_rows > 0, (u * E4M3_MAX) / a_rows, 0.0)
+    codes = e4m3_encode(np.clip(quot, -E4M3_MAX, E4M3_MAX))
     return codes, scale, y
 
 
@@ -278,7 +278,7 @@ def fp8_attention_emulate(qh, kh, vh, causal: bool = False, scale=None, Bc: int 
 
 
 def fp8_emulate(q, k, v, signs=None, mode: str = "block+had", causal: bool = False, scale=None, Bc: int = 64,
-                quantize: bool = True):
+                quantize: bool = True, v_pow2: bool = False):
     """End-to-end FP8 attention emulation in one of three scaling modes.
 
     mode:
@@ -286,8 +286,9 @@ def fp8_emulate(q, k, v, signs=None, mode: str = "block+had", causal: bool = Fal
       per-block scales for Q, K and V (the product path);
       ``"block"`` -- per-block scales, no rotation;
       ``"tensor"`` -- one scale per tensor, no rotation (the baseline).
-    With ``quantize=False`` every rounding step is skipped, which must give
-    plain attention (the rotation cancels in Q K^T).
+    V's scale is amax / 448 per block (or per tensor), or with ``v_pow2`` the
+    power-of-two variant.  With ``quantize=False`` every rounding step is
+    skipped, which must give plain attention (the rotation cancels in Q K^T).
     Returns float64 ``(o, lse)``.
     """
     if mode not in ("block+had", "block", "tensor"):
@@ -295,7 +296,7 @@ def fp8_emulate(q, k, v, signs=None, mode: str = "block+had", causal: bool = Fal
     rot = signs if mode == "block+had" else None
     per_tensor = mode == "tensor"
     out = []
-    for x, sg, p2 in ((q, rot, False), (k, rot, False), (v, None, True)):
+    for x, sg, p2 in ((q, rot, False), (k, rot, False), (v, None, bool(v_pow2))):
         codes, s, y = quantize_fp8(x, signs=sg, per_tensor=per_tensor, quantize=quantize, pow2=p2)
         out.append((dequantize_fp8(codes, s) if quantize else y, s))
     (qh, _), (kh, _), (vh, vs) = out

@@ -221,6 +221,40 @@ def test_p_quantisation_worked_example():
     np.testing.assert_allclose(lse[0, 0, 0], np.log(3.9), rtol=1e-12)
 
 
+def test_p_quantisation_worked_example_non_power_of_two_v_scale():
+    """The two-key case above with s_V = 3 = 1.5 * 2^1 (mu = 1.5): P = (3/4,
+    0.225) is brought to FP8 as P * 2^7 * 1.5 = (144, 43.2); 144 is on the
+    E4M3 grid and 43.2 rounds to 44 (step 4 in [32, 64)).  So P_q = (144,
+    44) / 192, l = 0.975 from the unrounded P, O = P_q V / l, lse = ln(3.9)."""
+    qh = np.ones((1, 1, 1, 1))
+    kh = np.array([np.log(3.0), np.log(3.0) + np.log(0.3)]).reshape(1, 1, 2, 1)
+    vh = np.eye(2).reshape(1, 1, 2, 2)
+    o, lse = fp8_attention_emulate(qh, kh, vh, scale=1.0, Bc=2, v_scale=np.full((1, 1, 1), 3.0), block=128)
+    np.testing.assert_allclose(o[0, 0, 0], [144 / 192 / 0.975, 44 / 192 / 0.975], rtol=1e-12)
+    np.testing.assert_allclose(lse[0, 0, 0], np.log(3.9), rtol=1e-12)
+
+
+def test_fp8_emulate_v_scale_variants():
+    """V's default block scale is amax / 448 (every non-zero block reaches
+    code 448); the power-of-two variant puts the block amax in (224, 448];
+    both emulations stay close to exact attention."""
+    g = np.random.default_rng(21)
+    B, H, N, d = 1, 2, 256, 64
+    q, k, v = (g.standard_normal((B, H, N, d)) for _ in range(3))
+    c_v, s_v, _ = quantize_fp8(v)
+    for b in range(B):
+        for h in range(H):
+            for i in range(2):
+                assert np.abs(e4m3_decode(c_v[b, h, i * 128:(i + 1) * 128])).max() == 448.0
+    mu = s_v / np.exp2(np.floor(np.log2(s_v)))
+    assert np.any(mu != 1.0)
+    o_ref, _ = attention_ref(q, k, v)
+    signs = g.choice([-1, 1], (H, d))
+    for v_pow2 in (False, True):
+        o, _ = fp8_emulate(q, k, v, signs=signs, Bc=64, v_pow2=v_pow2)
+        assert float(np.sqrt(np.mean((o - o_ref) ** 2))) < 2e-2
+
+
 def test_p_quantisation_invariant_to_the_power_of_two_reference():
     """E4M3 rounding commutes with powers of two in the normal range: shifting
     every score by a whole number of ln 2 moves the reference by the same
@@ -257,20 +291,52 @@ def test_p_quantisation_never_saturates():
     assert 2.0 ** 7 * mu < 256 and e4m3_round(2.0 ** 7 * mu) <= 256
 
 
-def test_code_decision_in_float32_differs_from_float64_only_at_ties():
-    # the fp32 decision agrees with exact rounding of u * 448 / amax except
-    # where the exact value sits (almost) on a rounding tie
+def _nearest_e4m3_exact(q):
+    """Brute force in exact rational arithmetic: the E4M3 magnitude nearest
+    to |q| (ties to the even code), with q clamped to +-448, signed."""
+    from fractions import Fraction
+
+    mags = [Fraction(float(v)) for v in e4m3_decode(np.arange(127, dtype=np.uint8))]
+    a = min(abs(q), Fraction(448))
+    best = min(range(127), key=lambda c: (abs(mags[c] - a), c % 2))
+    return -mags[best] if q < 0 else mags[best]
+
+
+def test_codes_are_the_nearest_e4m3_of_the_exact_quotient():
+    """Every code is the E4M3 value nearest to y / s = u * 448 / max|u|,
+    checked against brute force over all 127 magnitudes in exact rational
+    arithmetic (u and max|u| are exact in float64: sums of bf16 values)."""
+    from fractions import Fraction
+
     g = np.random.default_rng(11)
     x = torch.from_numpy(g.standard_normal((1, 2, 256, 128))).to(torch.bfloat16)
-    codes, s, y = quantize_fp8(x)
-    exact = e4m3_encode(np.clip(y / np.repeat(s, 128, axis=2)[:, :, :, None], -448, 448))
-    diff = e4m3_decode(codes) != e4m3_decode(exact)
-    assert diff.mean() < 5e-3
-    q = (y / np.repeat(s, 128, axis=2)[:, :, :, None])[diff]
-    vals = e4m3_decode(np.arange(127, dtype=np.uint8))
-    mids = (vals[1:] + vals[:-1]) / 2
-    near = np.min(np.abs(np.abs(q)[:, None] - mids[None, :]) / np.maximum(np.abs(q)[:, None], 1e-30), axis=1)
-    assert np.all(near < 1e-6)
+    signs = g.choice([-1, 1], (2, 128))
+    for sg in (None, signs):
+        codes, s, y = quantize_fp8(x, signs=sg)
+        r = np.sqrt(128) if sg is not None else 1.0
+        u = y * r  # the unnormalised rotation, exact
+        idx = g.integers(0, u.size, 3000)
+        for flat in idx:
+            b, h, n, c = np.unravel_index(flat, u.shape)
+            blk = np.abs(u[b, h, (n // 128) * 128:(n // 128 + 1) * 128]).max()
+            q = Fraction(float(u[b, h, n, c])) * 448 / Fraction(float(blk))
+            assert Fraction(float(e4m3_decode(codes[b, h, n, c]))) == _nearest_e4m3_exact(q)
+
+
+def test_codes_at_planted_ties_go_to_even():
+    """Block amax 448 (so y / s = y exactly) with entries on E4M3 rounding
+    ties: 1.0625 lies between 1 and 1.125 (even: 1), 1.1875 between 1.125
+    and 1.25 (even: 1.25), 232 between 224 and 240 (even: 224), and 0.0029296875
+    (1.5 * 2^-9) between the subnormals 2^-9 and 2^-8 (even: 2^-8)."""
+    x = np.zeros((1, 1, 128, 4))
+    x[0, 0, 0, 0] = 448.0
+    ties = [1.0625, 1.1875, 232.0, 1.5 * 2.0 ** -9, -1.0625, -232.0]
+    want = [1.0, 1.25, 224.0, 2.0 ** -8, -1.0, -224.0]
+    for i, t in enumerate(ties):
+        x[0, 0, 1 + i, 1] = t
+    codes, s, _ = quantize_fp8(x)
+    assert s[0, 0, 0] == 1.0
+    np.testing.assert_array_equal(e4m3_decode(codes[0, 0, 1:1 + len(ties), 1]), want)
 
 
 def test_pow2_scale_closed_form():
