@@ -284,38 +284,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 __device__ __forceinline__ int k8_swizzle(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int v8_swizzle(int d) { return (d >> 2) & 3; }
 
-// Instruction-group order of one forward step (compiler scheduling hints;
-// masks: 0x008 matrix, 0x100 LDS read, 0x002 vector ALU).  First block: the
-// K operand reads, then the four S_{j+1} products each followed by a share
-// of the softmax of S_j.  Second block: the V^T reads and the four PV
-// products with the row max of S_{j+1} between them.
-#ifndef FA8_SCHED
-#define FA8_SCHED 0
-#endif
-#ifndef FA8_VPM
-#define FA8_VPM 30
-#endif
-__device__ __forceinline__ void schedule_fp8_qk() {
-  if constexpr (FA8_SCHED) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, FA8_VPM, 0);
-    }
-  }
-}
-__device__ __forceinline__ void schedule_fp8_pv() {
-  if constexpr (FA8_SCHED) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-    }
-  }
-}
-
 template <bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
   constexpr int D = 128;
@@ -497,10 +465,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
       pb[w] = (int)cvt_e4m3x4(e0, e1, e2, e3);
     }
     const float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
-    schedule_fp8_qk();
     // The test also reads lsum and the last S_{j+1} product (finite scores:
     // adding 0 * s is exact), which keeps the products and the softmax in
-    // this block, ahead of the branch, for the interleave above.
+    // one block ahead of the branch, where the compiler interleaves them.
     if (__any(shift + 0.f * (s_out[0][15] + s_out[NKB - 1][15]) > 64.f && lsum >= 0.f)) {
       // rare (scores grew by more than 2^64 over the first tile's): move the
       // base so O and l stay far from the fp32 range; an exact power of two
@@ -527,7 +494,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
       o[db] = mfma_fp8_32x32x64(a, pb, o[db], v_exp, 127 - 7 + ishift);
     }
     mx = rowmax(s_out);
-    schedule_fp8_pv();
   };
 
   f32x16 sa[NKB], sb[NKB];
