@@ -287,9 +287,11 @@ def fp8_prep(x, signs=None, transpose: bool = False, per_tensor: bool = False, p
     return x8, sc
 
 
-def fp8_prep_v(v, per_tensor: bool = False, out=None, scale_out=None):
-    """The PV operand: V transposed with power-of-two block scales."""
-    return fp8_prep(v, transpose=True, per_tensor=per_tensor, pow2_scale=True, out=out, scale_out=scale_out)
+def fp8_prep_v(v, per_tensor: bool = False, pow2_scale: bool = False, out=None, scale_out=None):
+    """The PV operand: V transposed, never rotated, with block (or tensor)
+    scales amax / 448, or with ``pow2_scale`` the power-of-two variant
+    2^ceil(log2(amax / 448))."""
+    return fp8_prep(v, transpose=True, per_tensor=per_tensor, pow2_scale=pow2_scale, out=out, scale_out=scale_out)
 
 
 def fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, causal: bool = False, softmax_scale: float | None = None,

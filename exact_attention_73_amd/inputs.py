@@ -10,6 +10,15 @@ Recipe (CPU, deterministic; torch's Philox-free CPU generator):
   entries, which are replaced by ``10 * randn`` (N(0, 10^2)), all drawn from
   the same generator.  The pages' FP8 error study uses a synthetic
   distribution with a few large outliers without giving its parameters.
+* Channel-outlier inputs (a second FP8 error report): Q, K, V as above
+  (no scattered outliers); then, per head, two channels drawn with
+  ``randint(0, d, (H, 2))`` from ``Generator("cpu").manual_seed(seed + 2)``
+  are multiplied by 4 in both Q and K before the bf16 cast: outliers that
+  sit in the same channel of Q and K, the case the FA3 explainer's section
+  on incoherent processing describes.
+* Ramped keys (inputs whose row maxima keep growing from key tile to key
+  tile): K from any recipe above, row j of n (along the key axis) multiplied
+  by 1 + (top - 1) j / (n - 1) in float32, then cast back to bf16.
 * Upstream gradient dO (backward): ``torch.randn`` float32 ``[B, H, N, d]``
   from ``Generator("cpu").manual_seed(seed + 2)``, cast to bfloat16.
 * Rotation signs: ``[H, d]`` int8 of +-1 from ``randint(0, 2) * 2 - 1`` with
@@ -24,7 +33,8 @@ from dataclasses import dataclass, field
 
 import torch
 
-__all__ = ["make_qkv", "make_do", "make_signs", "softmax_scale", "Workload", "WORKLOADS", "sweep_workloads", "sweep_seed"]
+__all__ = ["make_qkv", "make_qkv_channel_outliers", "ramp_keys", "make_do", "make_signs", "softmax_scale", "Workload",
+           "WORKLOADS", "sweep_workloads", "sweep_seed"]
 
 
 def make_qkv(B: int, H: int, N: int, d: int, seed: int, outliers: bool = False, outlier_frac: float = 1e-3,
@@ -37,6 +47,29 @@ def make_qkv(B: int, H: int, N: int, d: int, seed: int, outliers: bool = False, 
             m = torch.rand(x.shape, generator=g) < outlier_frac
             x[m] = outlier_std * torch.randn(int(m.sum()), generator=g)
     return tuple(x.to(torch.bfloat16) for x in xs)
+
+
+def make_qkv_channel_outliers(B: int, H: int, N: int, d: int, seed: int, n_channels: int = 2,
+                              factor: float = 4.0):
+    """bf16 CPU ``(q, k, v)`` with ``n_channels`` seeded channels per head of
+    Q and K multiplied by ``factor`` (the same channels in both)."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    xs = [torch.randn((B, H, N, d), generator=g, dtype=torch.float32) for _ in range(3)]
+    gc = torch.Generator("cpu").manual_seed(int(seed) + 2)
+    ch = torch.randint(0, d, (H, n_channels), generator=gc)
+    for x in xs[:2]:
+        for h in range(H):
+            x[:, h, :, ch[h]] *= factor
+    return tuple(x.to(torch.bfloat16) for x in xs)
+
+
+def ramp_keys(k: torch.Tensor, top: float, axis: int = 2) -> torch.Tensor:
+    """k (bf16) with row j of the key axis scaled by 1 + (top - 1) j / (n - 1)."""
+    n = k.shape[axis]
+    f = 1.0 + (top - 1.0) * torch.arange(n, dtype=torch.float32) / max(n - 1, 1)
+    shape = [1] * k.dim()
+    shape[axis] = n
+    return (k.float() * f.reshape(shape)).to(torch.bfloat16)
 
 
 def make_do(B: int, H: int, N: int, d: int, seed: int) -> torch.Tensor:

@@ -62,7 +62,7 @@ enum fa_status {
 /* Flags of fa_fp8_prep. */
 #define FA_PREP_TRANSPOSE 1u  /* write x8 transposed, [B, H, d, fa_fp8_vt_ld(N)]       */
 #define FA_PREP_PER_TENSOR 2u /* one scale for the whole tensor (the comparison mode) */
-#define FA_PREP_POW2_SCALE 4u /* power-of-two scales (for V, the PV operand); no rotation */
+#define FA_PREP_POW2_SCALE 4u /* power-of-two scales (a variant for V, the PV operand); no rotation */
 
 /*
  * fa_fwd_bf16 -- exact attention forward, bf16 operands, fp32 accumulation.
@@ -114,14 +114,17 @@ int fa_fwd_bf16_gqa(const void* q, const void* k, const void* v, float* o, float
  *              cu_seqlens_k[b] .. cu_seqlens_k[b+1] - 1.  Values are clamped
  *              into [0, total] on the device, so no access leaves the tensors.
  *   max_seqlen_q : at least the largest query count of any sequence (sizes
- *              the grid; query rows beyond it are not written).
+ *              the grid).  The device cannot report a longer sequence: its
+ *              query rows beyond max_seqlen_q are left unwritten, so the
+ *              caller must pass the true maximum.
  *   Hq, Hkv, d, causal, softmax_scale : as fa_fwd_bf16_gqa, applied to each
  *              sequence on its own (causal bottom-right per sequence; a query
  *              that sees no key, e.g. in a sequence with no keys, gets o = 0
  *              and lse = -inf).  Empty sequences are allowed.
  *
  * Rows of o and lse that belong to no sequence are not written.
- * FA_ERR_SHAPE also when total_k * Hkv * d * 2 >= 2^31 or a size is negative;
+ * FA_ERR_SHAPE also when total_q * Hq * d * 2 or total_k * Hkv * d * 2 is
+ * >= 2^31 (rows are addressed with 32-bit byte offsets) or a size is negative;
  * FA_ERR_ALIGN when a cu_seqlens array is not 4-byte aligned.
  */
 int fa_fwd_bf16_varlen(const void* q, const void* k, const void* v, float* o, float* lse, const int* cu_seqlens_q,
@@ -243,17 +246,20 @@ int fa_bwd_bf16_gqa(const void* q, const void* k, const void* v, const float* o,
  *   x_scale : fp32 [B, H, ceil(N / 128)]: s = amax(|y|) / 448 over each block
  *             of 128 rows (all of d); s = 1 for an all-zero block.  With
  *             FA_PREP_POW2_SCALE, s = 2^ceil(log2(amax / 448)) instead (the
- *             smallest power of two with amax / s <= 448), which is what V
- *             should use: the PV product then takes s as an exact block
- *             exponent.  With FA_PREP_PER_TENSOR, amax runs over the whole
- *             tensor and every entry holds the same s.
+ *             smallest power of two with amax / s <= 448): a variant for V,
+ *             whose scale the PV product then takes as an exact block
+ *             exponent, at the cost of up to one bit of V's range.  With
+ *             FA_PREP_PER_TENSOR, amax runs over the whole tensor and every
+ *             entry holds the same s.
  *   d       : 128.
  *   flags   : OR of FA_PREP_TRANSPOSE, FA_PREP_PER_TENSOR and
  *             FA_PREP_POW2_SCALE (FA_ERR_ARG for any other bit, or for
  *             FA_PREP_POW2_SCALE together with signs).
  *
  * Codes are round-to-nearest-even of clamp(y * 448 / amax, -448, 448), the
- * product formed in fp32; with FA_PREP_POW2_SCALE of y / s (exact).
+ * product formed in fp32 (one code step from the exact quotient's rounding
+ * where that quotient lies within fp32 rounding of a tie); with
+ * FA_PREP_POW2_SCALE of y / s (exact).
  * Per-tensor mode issues three kernels on `stream` (block amaxes into
  * x_scale, quantise with the tensor amax reduced from them, then the
  * scales); block mode issues one.  Calls that share an x_scale buffer
@@ -280,8 +286,8 @@ int fa_fp8_vt_ld(int N);
  *   q8, k8  : uint8 [B, H, N, d]
  *   v8t     : uint8 [B, H, d, fa_fp8_vt_ld(N)] (padding columns must be 0)
  *   q_scale, k_scale, v_scale : fp32 [B, H, ceil(N / 128)], positive
- *             normal floats (v_scale from FA_PREP_POW2_SCALE, so that
- *             mu_j = 1; other positive scales are accepted)
+ *             normal floats (as fa_fp8_prep writes them: amax / 448, or
+ *             powers of two with FA_PREP_POW2_SCALE, where mu_j = 1)
  *   o, lse  : as in fa_fwd_bf16
  *   d       : 128.
  */

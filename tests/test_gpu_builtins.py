@@ -217,3 +217,90 @@ def test_buffer_load_lds_placement_and_range(probes):
             np.testing.assert_array_equal(got[l], np.arange(4) + perm[l] * 4)
         else:
             np.testing.assert_array_equal(got[l], 0)
+
+
+def _mfma_fp8_run(probes, A, B, sa=127, sb=127):
+    a = np.zeros((64, 32), np.uint8)
+    b = np.zeros((64, 32), np.uint8)
+    for l in range(64):
+        a[l] = A[l % 32, 32 * (l // 32): 32 * (l // 32) + 32]
+        b[l] = B[32 * (l // 32): 32 * (l // 32) + 32, l % 32]
+    c = torch.zeros(64, 16, dtype=torch.float32, device="cuda")
+    assert probes.probe_mfma_fp8(_p(torch.from_numpy(a).cuda()), _p(torch.from_numpy(b).cuda()), _p(c), sa, sb,
+                                 _s()) == 0
+    torch.cuda.synchronize()
+    cc = c.cpu().numpy()
+    got = np.zeros((32, 32))
+    for l in range(64):
+        for r in range(16):
+            got[8 * (r // 4) + 4 * (l // 32) + (r % 4), l % 32] = cc[l, r]
+    return got
+
+
+FP8_ACC_EPS = 2.0 ** -11  # bound on the FP8 product's measured accumulation error (see below)
+
+
+@pytest.mark.parametrize("codes", ["full_range", "full_range_signed", "block_scaled_gaussian"])
+def test_mfma_fp8_accumulation_error(probes, codes):
+    """Error of one 64-term FP8 product sum against the exact sum, relative
+    to sum |a_k b_k| (the scale of an accumulation error).  The matrix core
+    does not keep every bit of a 64-product sum: on codes spanning the whole
+    E4M3 range the error reaches about 2^-11.9 of sum |a_k b_k| (2^-12.4
+    with random signs), far above fp32 rounding.  This bounds how closely
+    FP8 scores of large magnitude can match an exact emulation; recorded
+    here, gated at 2^-11."""
+    worst = 0.0
+    for seed in range(4):
+        rng = np.random.default_rng(100 + seed)
+        if codes == "block_scaled_gaussian":
+            A = e4m3_encode(np.clip(rng.standard_normal((32, 64)) * 112, -448, 448))
+            B = e4m3_encode(np.clip(rng.standard_normal((64, 32)) * 112, -448, 448))
+        else:
+            A = rng.integers(0, 0x7F, size=(32, 64)).astype(np.uint8)
+            B = rng.integers(0, 0x7F, size=(64, 32)).astype(np.uint8)
+            if codes == "full_range_signed":
+                A |= (rng.integers(0, 2, size=A.shape) * 0x80).astype(np.uint8)
+                B |= (rng.integers(0, 2, size=B.shape) * 0x80).astype(np.uint8)
+        got = _mfma_fp8_run(probes, A, B)
+        Ad, Bd = e4m3_decode(A), e4m3_decode(B)
+        ref = Ad @ Bd
+        mag = np.abs(Ad) @ np.abs(Bd)
+        worst = max(worst, float(np.max(np.abs(got - ref) / mag)))
+    msg = f"fp8 mfma accumulation error / sum|ab| ({codes}): {worst:.3e} = 2^{np.log2(max(worst, 1e-300)):.2f}"
+    print(msg)
+    os.makedirs("gpurun_out", exist_ok=True)
+    with open("gpurun_out/mfma_accumulation.txt", "a") as f:
+        f.write(msg + "\n")
+    assert worst <= FP8_ACC_EPS
+
+
+def test_mfma_bf16_accumulation_error(probes):
+    """The same measurement for one 16-term bf16 product sum."""
+    worst = 0.0
+    for seed in range(4):
+        g = torch.Generator().manual_seed(200 + seed)
+        A = (torch.randn(32, 16, generator=g) * torch.exp2(torch.randint(-8, 8, (32, 16), generator=g))).to(torch.bfloat16)
+        B = (torch.randn(16, 32, generator=g) * torch.exp2(torch.randint(-8, 8, (16, 32), generator=g))).to(torch.bfloat16)
+        a = torch.zeros(64, 8, dtype=torch.bfloat16)
+        b = torch.zeros(64, 8, dtype=torch.bfloat16)
+        for l in range(64):
+            a[l] = A[l % 32, 8 * (l // 32): 8 * (l // 32) + 8]
+            b[l] = B[8 * (l // 32): 8 * (l // 32) + 8, l % 32]
+        c = torch.zeros(64, 16, dtype=torch.float32, device="cuda")
+        assert probes.probe_mfma_bf16(_p(a.cuda()), _p(b.cuda()), _p(c), _s()) == 0
+        torch.cuda.synchronize()
+        cc = c.cpu().numpy()
+        got = np.zeros((32, 32))
+        for l in range(64):
+            for r in range(16):
+                got[8 * (r // 4) + 4 * (l // 32) + (r % 4), l % 32] = cc[l, r]
+        Ad, Bd = A.double().numpy(), B.double().numpy()
+        ref = Ad @ Bd
+        mag = np.abs(Ad) @ np.abs(Bd)
+        worst = max(worst, float(np.max(np.abs(got - ref) / mag)))
+    msg = f"bf16 mfma accumulation error / sum|ab|: {worst:.3e} = 2^{np.log2(max(worst, 1e-300)):.2f}"
+    print(msg)
+    os.makedirs("gpurun_out", exist_ok=True)
+    with open("gpurun_out/mfma_accumulation.txt", "a") as f:
+        f.write(msg + "\n")
+    assert worst <= 2.0 ** -20
