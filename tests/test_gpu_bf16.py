@@ -3,7 +3,7 @@
 Bar (the numeric gates of the bf16 path): max-abs <= 1e-2 and RMSE <= 2e-3 on
 N(0, 1) inputs, plus relative RMSE <= 1e-2 and lse max-abs <= 1e-3 (the
 absolute gates alone are loose: rms(O) is about sqrt(e / N) for N(0, 1)
-inputs, 0.026 at N = 4096).  The kernel rounds P to bf16 (relative 2^-9)
+inputs, 0.026 at N = 4096).  The kernel rounds P to bf16 (8 significant bits, relative 2^-8)
 before the PV product, which is the dominant error; expected values are a
 few 1e-3 relative.
 """

@@ -1,7 +1,7 @@
 """GPU parity of fa_bwd_bf16 (dQ, dK, dV) against the fp64 oracle.
 
 The GPU backward recomputes P from bf16 Q, K with the forward's fp32 lse and
-rounds P and dS to bf16 for its matrix products (relative 2^-9 per
+rounds P and dS to bf16 for its matrix products (relative 2^-8 per
 element); dV, dK, dQ are sums of such terms with fp32 accumulation.  Gates,
 per gradient against the fp64 gradients of the same bf16 inputs: relative
 RMSE <= 1e-2 and max-abs error <= 2e-2 of the largest reference magnitude.
