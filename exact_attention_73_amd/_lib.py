@@ -77,6 +77,17 @@ def _need(t: torch.Tensor, dtype, name: str):
         raise ValueError(f"{name} must be a contiguous {dtype} tensor on a GPU")
 
 
+def _out(t, shape, dtype, device, name):
+    """A new output tensor, or the caller's after checking dtype, device,
+    contiguity and shape (a short buffer would be an out-of-bounds write)."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _need(t, dtype, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
 def fwd_bf16(q, k, v, causal: bool = False, softmax_scale: float | None = None, out=None, lse=None):
     """O, lse = attention(q, k, v) for bf16 ``[B, H, N, d]`` CUDA tensors.
 
@@ -88,10 +99,8 @@ def fwd_bf16(q, k, v, causal: bool = False, softmax_scale: float | None = None, 
         raise ValueError("q, k, v must share one shape [B, H, N, d]")
     B, H, N, d = q.shape
     scale = (1.0 / d ** 0.5) if softmax_scale is None else float(softmax_scale)
-    o = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if out is None else out
-    ls = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    _need(o, torch.float32, "out")
-    _need(ls, torch.float32, "lse")
+    o = _out(out, (B, H, N, d), torch.float32, q.device, "out")
+    ls = _out(lse, (B, H, N), torch.float32, q.device, "lse")
     st = load().fa_fwd_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), ls.data_ptr(), B, H, N, d,
                             int(bool(causal)), scale, _stream(q))
     _check("fa_fwd_bf16", st)
@@ -107,10 +116,8 @@ def fwd_bf16_gqa(q, k, v, causal: bool = False, softmax_scale: float | None = No
     bottom-right causal alignment. Returns fp32 ``o [B, Hq, Nq, d]``, ``lse [B, Hq, Nq]``."""
     B, Hq, Hkv, Nq, Nk, d = _gqa_shapes(q, k, v)
     scale = (1.0 / d ** 0.5) if softmax_scale is None else float(softmax_scale)
-    o = torch.empty((B, Hq, Nq, d), dtype=torch.float32, device=q.device) if out is None else out
-    ls = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
-    _need(o, torch.float32, "out")
-    _need(ls, torch.float32, "lse")
+    o = _out(out, (B, Hq, Nq, d), torch.float32, q.device, "out")
+    ls = _out(lse, (B, Hq, Nq), torch.float32, q.device, "lse")
     st = load().fa_fwd_bf16_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), ls.data_ptr(), B, Hq, Hkv,
                                 Nq, Nk, d, int(bool(causal)), scale, _stream(q))
     _check("fa_fwd_bf16_gqa", st)
@@ -143,10 +150,8 @@ def fwd_bf16_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, caus
     total_k, Hkv = k.shape[0], k.shape[1]
     B = cu_seqlens_q.numel() - 1
     scale = (1.0 / d ** 0.5) if softmax_scale is None else float(softmax_scale)
-    o = torch.empty((total_q, Hq, d), dtype=torch.float32, device=q.device) if out is None else out
-    ls = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device) if lse is None else lse
-    _need(o, torch.float32, "out")
-    _need(ls, torch.float32, "lse")
+    o = _out(out, (total_q, Hq, d), torch.float32, q.device, "out")
+    ls = _out(lse, (Hq, total_q), torch.float32, q.device, "lse")
     st = load().fa_fwd_bf16_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), ls.data_ptr(),
                                    cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, Hq, Hkv, total_q, total_k,
                                    int(max_seqlen_q), d, int(bool(causal)), scale, _stream(q))
@@ -191,10 +196,8 @@ def fwd_bf16_decode(q, k, v, causal: bool = False, softmax_scale: float | None =
         if not workspace.is_cuda or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous tensor on a GPU")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    o = torch.empty((B, Hq, Nq, d), dtype=torch.float32, device=q.device) if out is None else out
-    ls = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
-    _need(o, torch.float32, "out")
-    _need(ls, torch.float32, "lse")
+    o = _out(out, (B, Hq, Nq, d), torch.float32, q.device, "out")
+    ls = _out(lse, (B, Hq, Nq), torch.float32, q.device, "lse")
     st = load().fa_fwd_bf16_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), ls.data_ptr(), B, Hq,
                                    Hkv, Nq, Nk, d, int(bool(causal)), scale, splits, ws_ptr, ws_bytes, _stream(q))
     _check("fa_fwd_bf16_decode", st)
@@ -260,7 +263,7 @@ def fp8_prep(x, signs=None, transpose: bool = False, per_tensor: bool = False, p
     """E4M3 codes and per-128-row scales of one bf16 ``[B, H, N, d]`` tensor.
 
     ``signs``: int8 ``[H, d]`` of +-1 on the GPU (rotate, for Q and K) or None.
-    For V use ``transpose=True, pow2_scale=True`` (:func:`fp8_prep_v`).
+    For V use ``transpose=True`` without signs (:func:`fp8_prep_v`).
     Returns ``(x8, scale)``: uint8 ``[B, H, N, d]`` (or ``[B, H, d, ld]`` when
     ``transpose``) and fp32 ``[B, H, ceil(N / 128)]``, written into ``out`` and
     ``scale_out`` when given.
@@ -309,10 +312,8 @@ def fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, causal: bool = False, softma
         if tuple(t.shape) != (B, H, nb):
             raise ValueError("scales must be [B, H, ceil(N / 128)]")
     scale = (1.0 / d ** 0.5) if softmax_scale is None else float(softmax_scale)
-    o = torch.empty((B, H, N, d), dtype=torch.float32, device=q8.device) if out is None else out
-    ls = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if lse is None else lse
-    _need(o, torch.float32, "out")
-    _need(ls, torch.float32, "lse")
+    o = _out(out, (B, H, N, d), torch.float32, q8.device, "out")
+    ls = _out(lse, (B, H, N), torch.float32, q8.device, "lse")
     st = load().fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8t.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(),
                            v_scale.data_ptr(), o.data_ptr(), ls.data_ptr(), B, H, N, d, int(bool(causal)), scale,
                            _stream(q8))

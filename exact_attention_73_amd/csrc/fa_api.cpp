@@ -182,8 +182,10 @@ int fa_fwd_bf16_varlen(const void* q, const void* k, const void* v, float* o, fl
   const bool dok = d == 64 || d == 128 || d == 256;
   const double dd = dok ? d : 1;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || total_q < 0 || total_k < 0 || max_seqlen_q < 0) return FA_ERR_SHAPE;
-  // K/V rows of one sequence are addressed with 32-bit byte offsets
+  // Q and K/V rows of one sequence are addressed with 32-bit byte offsets
+  // (a sequence's rows lie inside the packed tensors)
   if ((double)total_k * Hkv * dd * 2.0 >= 2147483648.0) return FA_ERR_SHAPE;
+  if ((double)total_q * Hq * dd * 2.0 >= 2147483648.0) return FA_ERR_SHAPE;
   if ((double)total_q * Hq * dd >= 1099511627776.0) return FA_ERR_SHAPE;  // 2^40 elements
   if ((double)B * Hq * (((double)max_seqlen_q + 127) / 128) >= 2147483647.0) return FA_ERR_SHAPE;
   if (!dok) return FA_ERR_HEADDIM;
