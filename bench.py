@@ -1,35 +1,40 @@
 #!/usr/bin/env python3
 """Forward-attention throughput on one MI355X.
 
-One step = the bf16 exact-attention forward on the standard block
-(B=4, H=16, N=2048, d=128, bf16 N(0, 1) inputs, scale 1/sqrt(d)), run once
-non-causal and once causal, inputs resident in HBM.  FLOPs are counted as
-4 B H N^2 d per forward, halved for causal.  The JSON line also carries:
+One step = the bf16 exact-attention forward at d = 128 and N = 4096 on the
+sequence-length sweep's 16384-token batch (B=4, H=16, bf16 N(0, 1) inputs,
+seed 73212, scale 1/sqrt(d)), run once non-causal and once causal, inputs
+resident in HBM.  FLOPs are counted as 4 B H N^2 d per forward, halved for
+causal.  The JSON line also carries:
 
-* ``roofline`` of the dominant kernel (the non-causal bf16 forward), whose
-  average launch duration is measured with HIP events on the stream the
-  kernel runs on, against the dense bf16 MFMA peak (2516.6 TFLOP/s);
-* ``legs``: per-kernel figures -- the sequence-length sweeps at 16384 total
-  tokens for d = 128, 64 and 256 (TFLOPS and fraction of peak vs N, both
-  causal flags, plus the algorithmic HBM rate for N <= 1024), the long causal
-  context (B1 H16 N65536 d128), and the FP8 workload (B4 H16 N4096 d128):
-  prep GB/s and FP8 forward TFLOPS against the FP8 peak.  Legs time 30
-  launches after 10 warm-ups (5 after 1 for the long context) and give the
-  mean plus the rates at the p90/median/p10 durations; N = 512 and the prep
-  kernels are also timed with cold caches (a 1 GiB write before each launch);
-  and the backward (delta, dK/dV and dQ kernels per call) at B4 H16 N2048 and
-  N4096 d128 and N2048 d64, counted as 2.5 x the forward's FLOPs;
+* ``roofline`` of the dominant kernel (the non-causal bf16 forward of the
+  step), whose average launch duration is measured with HIP events on the
+  stream the kernel runs on, against the dense bf16 MFMA peak (2516.6
+  TFLOP/s);
+* ``config.fp8``: the FP8 workload (B4 H16 N4096 d128, 0.1 % outliers,
+  per-128-row amax / 448 block scales, Hadamard-rotated Q and K): forward
+  TFLOPS and its fraction of the FP8 peak (5033.2 TFLOP/s), prep GB/s and
+  the end-to-end rate, from the ``fp8`` leg;
+* ``legs``: per-kernel figures -- the standard block (B4 H16 N2048 d128),
+  the sequence-length sweeps at 16384 total tokens for d = 128, 64 and 256
+  (TFLOPS and fraction of peak vs N, both causal flags, plus the
+  algorithmic HBM rate for N <= 1024), the long causal context (B1 H16
+  N65536 d128), the FP8 workload (also with power-of-two V scales), the
+  backward, decode and packed-batch shapes.  Legs time 30 launches after 10
+  warm-ups (5 after 1 for the long context) and give the mean plus the rates
+  at the p90/median/p10 durations; N = 512 and the prep kernels are also
+  timed with cold caches (a 1 GiB write before each launch);
 * ``cpu_baseline``: the CPU fp64 oracle timed on a bounded sample of the
-  same step on this host.
+  same step on this host (core count and CPU model recorded).
 
 ``roofline.traffic`` is the kernel's HBM bytes per launch read by two
 rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE, each scaled by what the
 counter reads for a 256 MiB device copy), recorded in
-profiles/fwd_bf16_std_noncausal_traffic.md together with the SHA-256 of the
-kernel's sources; it is null when those sources changed since.
+profiles/fwd_bf16_N4096_noncausal_traffic.md together with the SHA-256 of
+the kernel's sources; it is null when those sources changed since.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
-                       [--legs sweep,sweep64,sweep256,long,fp8,bwd] [--copy-calibration]
+                       [--legs std,sweep,sweep64,sweep256,long,fp8,bwd,decode,varlen] [--copy-calibration]
 """
 
 from __future__ import annotations
@@ -48,12 +53,12 @@ GPU_HOLD_CYCLES = 20_000_000  # a short device-side spin before each timed regio
 ROOT = os.path.dirname(os.path.abspath(__file__))
 # HBM traffic of the dominant kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # passes; valid only while the kernel sources hash to what was profiled
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_bf16_std_noncausal_traffic.md")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_bf16_N4096_noncausal_traffic.md")
 TRAFFIC_SOURCES = ("exact_attention_73_amd/csrc/fa_fwd_bf16.hip", "exact_attention_73_amd/csrc/fa_device.h")
 COPY_CALIBRATION_BYTES = 256 << 20
 
 
-ALL_LEGS = ("sweep", "sweep64", "sweep256", "long", "fp8", "bwd", "decode", "varlen")
+ALL_LEGS = ("std", "sweep", "sweep64", "sweep256", "long", "fp8", "bwd", "decode", "varlen")
 
 
 def fwd_bytes(B, H, N, d):
@@ -174,10 +179,12 @@ def main():
     from exact_attention_73_amd.inputs import (WORKLOADS, make_do, make_qkv, make_signs, packed_batch_lengths,
                                               softmax_scale, sweep_workloads)
 
+    HEADLINE = next(x for x in sweep_workloads() if x.d == 128 and x.N == 4096)
+
     fa.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = WORKLOADS["std"]
+    w = HEADLINE
     B, H, N, d = w.B, w.H, w.N, w.d
     q, k, v = (x.to(dev) for x in make_qkv(B, H, N, d, w.seed))
     sc = softmax_scale(d)
@@ -214,10 +221,10 @@ def main():
     achieved = fwd_flops(B, H, N, d, False) / t_nc / 1e12
 
     legs = {
-        "bf16_std_noncausal_tflops": round(achieved, 2),
-        "bf16_std_causal_tflops": round(fwd_flops(B, H, N, d, True) / t_ca / 1e12, 2),
-        "bf16_std_noncausal_us": round(t_nc * 1e6, 2),
-        "bf16_std_causal_us": round(t_ca * 1e6, 2),
+        "step_noncausal_tflops": round(achieved, 2),
+        "step_causal_tflops": round(fwd_flops(B, H, N, d, True) / t_ca / 1e12, 2),
+        "step_noncausal_us": round(t_nc * 1e6, 2),
+        "step_causal_us": round(t_ca * 1e6, 2),
     }
     del q, k, v
 
@@ -235,6 +242,20 @@ def main():
         if scratch is None:
             scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         scratch.fill_(1.0)
+
+    if "std" in legs_on:
+        ws_ = WORKLOADS["std"]
+        qs, ks, vs = (x.to(dev) for x in make_qkv(ws_.B, ws_.H, ws_.N, ws_.d, ws_.seed))
+        row = {"workload": f"B{ws_.B} H{ws_.H} N{ws_.N} d{ws_.d}"}
+        for causal in (False, True):
+            st = _time_launches(lambda: fa.fwd_bf16(qs, ks, vs, causal=causal), 30, 10)
+            fl = fwd_flops(ws_.B, ws_.H, ws_.N, ws_.d, causal)
+            key = "causal" if causal else "noncausal"
+            row[key + "_tflops"] = round(fl / st["mean"] / 1e12, 1)
+            row[key + "_frac"] = round(fl / st["mean"] / 1e12 / PEAK_BF16, 4)
+            row[key + "_us"] = round(st["mean"] * 1e6, 2)
+        legs["bf16_std"] = row
+        del qs, ks, vs
 
     for dd, name in ((128, "sweep"), (64, "sweep64"), (256, "sweep256")):
         if name not in legs_on:
@@ -294,16 +315,20 @@ def main():
         l8 = torch.empty((w8.B, w8.H, w8.N), dtype=torch.float32, device=dev)
         t8 = _time_launches(lambda: fa.fwd_fp8(q8, k8, v8t, qs_, ks_, vs_, out=o8, lse=l8), 30, 10)
         t8c = _time_launches(lambda: fa.fwd_fp8(q8, k8, v8t, qs_, ks_, vs_, causal=True, out=o8, lse=l8), 30, 10)
+        v8p, vsp = fa.fp8_prep_v(v, pow2_scale=True)
+        t8p = _time_launches(lambda: fa.fwd_fp8(q8, k8, v8p, qs_, ks_, vsp, out=o8, lse=l8), 30, 10)
         elems = w8.B * w8.H * w8.N * w8.d
         prep_bytes = elems * 2 + elems + w8.B * w8.H * ((w8.N + 127) // 128) * 4
         f8 = fwd_flops(w8.B, w8.H, w8.N, w8.d, False)
         tb = _time_launches(lambda: fa.fwd_bf16(q, k, v, out=o8, lse=l8), 30, 10)
         legs["fp8"] = {
-            "workload": "B4 H16 N4096 d128 non-causal, 0.1% N(0,10^2) outliers",
+            "workload": "B4 H16 N4096 d128 non-causal, 0.1% N(0,10^2) outliers, per-128-row amax/448 block scales, "
+                        "Hadamard-rotated Q and K",
             "fwd_fp8_tflops": round(f8 / t8["mean"] / 1e12, 1),
             "fwd_fp8_frac_of_fp8_peak": round(f8 / t8["mean"] / 1e12 / PEAK_FP8, 4),
             "fwd_fp8_tflops_p10_p50_p90": _rates(f8, t8, 1e12),
             "fwd_fp8_causal_tflops": round(f8 / 2 / t8c["mean"] / 1e12, 1),
+            "fwd_fp8_vpow2_tflops": round(f8 / t8p["mean"] / 1e12, 1),
             "fwd_bf16_same_shape_tflops": round(f8 / tb["mean"] / 1e12, 1),
             "prep_qk_rotated_gbps": round(prep_bytes / t_prep["mean"] / 1e9, 1),
             "prep_qk_rotated_frac_of_hbm": round(prep_bytes / t_prep["mean"] / 1e9 / PEAK_HBM, 4),
@@ -312,7 +337,7 @@ def main():
             "prep_v_transposed_cold_gbps": round(prep_bytes / c_prep_v["mean"] / 1e9, 1),
             "end_to_end_tflops": round(f8 / (t8["mean"] + 2 * t_prep["mean"] + t_prep_v["mean"]) / 1e12, 1),
         }
-        del q, k, v, q8, k8, v8t, o8, l8
+        del q, k, v, q8, k8, v8t, v8p, o8, l8
     scratch = None
 
     if "bwd" in legs_on:
@@ -419,16 +444,21 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "standard block B4 H16 N2048 d128, bf16 forward, non-causal + causal per step",
-            "B": B, "H": H, "N": N, "d": d, "causal": [False, True],
+            "workload": "sequence-length sweep point B4 H16 N4096 d128 (16384 tokens), bf16 forward, "
+                        "non-causal + causal per step",
+            "B": B, "H": H, "N": N, "d": d, "causal": [False, True], "seed": w.seed,
             "flop_convention": "4*B*H*N^2*d per forward, halved for causal",
             "device": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count,
             "torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
             "host_wall_s": round(wall, 4),
+            "fp8": ({k_: legs["fp8"][k_] for k_ in ("workload", "fwd_fp8_tflops", "fwd_fp8_frac_of_fp8_peak",
+                                                    "fwd_fp8_causal_tflops", "fwd_fp8_vpow2_tflops",
+                                                    "prep_qk_rotated_gbps", "prep_v_transposed_gbps",
+                                                    "end_to_end_tflops")} if "fp8" in legs else None),
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "fwd_bf16_pp_kernel<non-causal> (d = 128 ping-pong)",
+            "kernel": "fwd_bf16_pp_kernel<128, non-causal> at B4 H16 N4096 d128",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16,
             "unit": "TFLOP/s",
@@ -483,10 +513,21 @@ def cpu_baseline(B, H, N, d, seed):
         t = run_heads(nh)
         desc = f"{nh} of {B * H} heads of one step"
     flops = (fwd_flops(1, nh, N, d, False) + fwd_flops(1, nh, N, d, True))
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": round(flops / t / 1e12, 6),
         "unit": "TFLOPS",
         "cores": int(threads),
+        "cpu_model": model,
+        "host_logical_cpus": os.cpu_count(),
         "kind": "oracle",
         "sample": f"{desc} (non-causal + causal), fp64 NumPy, {t:.2f} s; the oracle evaluates full score rows, "
                   f"so causal does twice the counted work",
