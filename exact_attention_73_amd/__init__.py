@@ -16,11 +16,12 @@ from ._lib import (  # noqa: F401
     fp8_vt_ld,
     fwd_bf16,
     fwd_bf16_decode,
+    fwd_bf16_decode_noalloc,
     fwd_bf16_gqa,
     fwd_bf16_varlen,
     fwd_fp8,
     load,
 )
 
-__all__ = ["fwd_bf16", "fwd_bf16_gqa", "fwd_bf16_varlen", "fwd_bf16_decode", "decode_splits", "decode_workspace_bytes",
+__all__ = ["fwd_bf16", "fwd_bf16_gqa", "fwd_bf16_varlen", "fwd_bf16_decode", "fwd_bf16_decode_noalloc", "decode_splits", "decode_workspace_bytes",
            "bwd_bf16", "bwd_bf16_gqa", "fp8_prep", "fp8_prep_v", "fwd_fp8", "fp8_vt_ld", "load", "FaError"]

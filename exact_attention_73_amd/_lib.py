@@ -30,6 +30,7 @@ SIGNATURES = {
     "fa_fwd_bf16_decode_splits": (_I, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "fa_fwd_bf16_decode_workspace": (_LL, [_I, _I, _I, _I, _I]),
     "fa_fwd_bf16_decode": (_I, [_VP, _VP, _VP, _FP, _FP, _I, _I, _I, _I, _I, _I, _I, _F, _I, _VP, _LL, _VP]),
+    "fa_fwd_bf16_decode_noalloc": (_I, [_VP, _VP, _VP, _FP, _FP, _I, _I, _I, _I, _I, _I, _I, _F, _I, _VP]),
     "fa_bwd_bf16_gqa": (_I, [_VP, _VP, _VP, _FP, _FP, _VP, _FP, _FP, _FP, _FP, _I, _I, _I, _I, _I, _I, _F, _VP]),
     "fa_bwd_bf16": (_I, [_VP, _VP, _VP, _FP, _FP, _VP, _FP, _FP, _FP, _FP, _I, _I, _I, _I, _I, _F, _VP]),
     "fa_fp8_prep": (_I, [_VP, _VP, _FP, _VP, _I, _I, _I, _I, ctypes.c_uint, _VP]),
@@ -201,6 +202,23 @@ def fwd_bf16_decode(q, k, v, causal: bool = False, softmax_scale: float | None =
     st = load().fa_fwd_bf16_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), ls.data_ptr(), B, Hq,
                                    Hkv, Nq, Nk, d, int(bool(causal)), scale, splits, ws_ptr, ws_bytes, _stream(q))
     _check("fa_fwd_bf16_decode", st)
+    return o, ls
+
+
+def fwd_bf16_decode_noalloc(q, k, v, causal: bool = False, softmax_scale: float | None = None, num_splits: int = 0,
+                            out=None, lse=None):
+    """``fwd_bf16_decode`` without a workspace: the chunk partials go to the
+    library's static per-device scratch buffer (16 MiB), so the call itself
+    allocates no device memory (pass ``out`` and ``lse`` for that).
+    ``num_splits`` 0 lets the library choose a count whose partials fit;
+    calls that overlap in time on one device race on the shared buffer."""
+    B, Hq, Hkv, Nq, Nk, d = _gqa_shapes(q, k, v)
+    scale = (1.0 / d ** 0.5) if softmax_scale is None else float(softmax_scale)
+    o = _out(out, (B, Hq, Nq, d), torch.float32, q.device, "out")
+    ls = _out(lse, (B, Hq, Nq), torch.float32, q.device, "lse")
+    st = load().fa_fwd_bf16_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), ls.data_ptr(), B,
+                                           Hq, Hkv, Nq, Nk, d, int(bool(causal)), scale, int(num_splits), _stream(q))
+    _check("fa_fwd_bf16_decode_noalloc", st)
     return o, ls
 
 

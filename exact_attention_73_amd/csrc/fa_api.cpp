@@ -113,6 +113,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_DEVICE: return "no HIP device, or the current device is not gfx950";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than the split count needs";
+    case FA_ERR_SCRATCH: return "the split count needs more partial-result memory than the static 16 MiB scratch buffer holds";
     default: return "unknown status";
   }
 }
@@ -263,6 +264,41 @@ int fa_fwd_bf16_decode(const void* q, const void* k, const void* v, float* o, fl
   p.scale = softmax_scale;
   p.c = softmax_scale * 1.4426950408889634f;
   return launch_status(fa::launch_dec_bf16(p, d, causal == 1, static_cast<hipStream_t>(stream)));
+}
+
+int fa_fwd_bf16_decode_noalloc(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Hq,
+                               int Hkv, int Nq, int Nk, int d, int causal, float softmax_scale, int num_splits,
+                               void* stream) {
+  static_assert(FA_DECODE_SCRATCH_BYTES == fa::kDecScratchBytes, "header and library agree on the buffer size");
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_PTR;
+  if (int e = check_decode_shape(B, Hq, Hkv, Nq, Nk, d)) return e;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (int e = check_scale(softmax_scale)) return e;
+  if (num_splits < 0) return FA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  if (int e = check_device()) return e;
+  int splits;
+  if (num_splits >= 1) {
+    splits = fa::dec_bf16_splits(B, Hq, Hkv, Nq, Nk, d, num_splits, 0);
+    if (decode_workspace_bytes(B, Hq, Nq, d, splits) > fa::kDecScratchBytes) return FA_ERR_SCRATCH;
+  } else {
+    const int cus = device_cus();
+    if (cus < 1) return FA_ERR_DEVICE;
+    splits = fa::dec_bf16_splits(B, Hq, Hkv, Nq, Nk, d, 0, cus);
+    while (splits > 1 && decode_workspace_bytes(B, Hq, Nq, d, splits) > fa::kDecScratchBytes)
+      splits = fa::dec_bf16_splits(B, Hq, Hkv, Nq, Nk, d, splits - 1, 0);
+  }
+  void* ws = nullptr;
+  if (splits > 1) {
+    if (fa::dec_scratch(&ws) != hipSuccess) {
+      (void)hipGetLastError();
+      return FA_ERR_DEVICE;
+    }
+  }
+  // the workspace entry point with the same effective count: it checks the
+  // rest and launches the same kernels
+  return fa_fwd_bf16_decode(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, softmax_scale, splits, ws,
+                            splits > 1 ? fa::kDecScratchBytes : 0, stream);
 }
 
 }  // extern "C"

@@ -38,6 +38,7 @@
 // order of the P^T registers matches the order of those reads.  With at
 // most 32 useful rows per product, the matrix cores idle most of the time;
 // the kernel is bound by HBM reads of K and V.
+#include <atomic>
 #include <cmath>
 
 #include "fa_device.h"
@@ -410,6 +411,36 @@ hipError_t launch(const DecBf16Params& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Device memory for the chunk partials of decode calls that bring no
+// workspace (fa_fwd_bf16_decode_noalloc).  Each device the library runs on
+// holds its own copy until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address comes only from
+// hipGetSymbolAddress with the device current (dec_scratch below).
+static __device__ __align__(256) unsigned char scratch[kDecScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch[kMaxScratchDevices];
+}  // namespace
+
+hipError_t dec_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  void* a = g_scratch[dev].load(std::memory_order_acquire);
+  if (a == nullptr) {
+    // once per device, with that device current; two threads racing here
+    // look up and store the same address
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (a == nullptr) return hipErrorInvalidSymbol;
+    g_scratch[dev].store(a, std::memory_order_release);
+  }
+  *ptr = a;
+  return hipSuccess;
+}
 
 hipError_t launch_dec_bf16(const DecBf16Params& p, int d, bool causal, hipStream_t stream) {
   switch (d) {

@@ -45,6 +45,11 @@ struct DecBf16Params {
 };
 
 hipError_t launch_dec_bf16(const DecBf16Params& p, int d, bool causal, hipStream_t stream);
+// Bytes of the library's static per-device scratch buffer for decode
+// partials, and its device address on the current device (looked up once
+// per device).
+constexpr long long kDecScratchBytes = 16ll << 20;
+hipError_t dec_scratch(void** ptr);
 // Key chunks per KV head: `requested` >= 1 reduced to the non-empty count,
 // or 0 for the cost model's choice on a device with num_cus compute units.
 int dec_bf16_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int requested, int num_cus);

@@ -16,9 +16,10 @@
  * ---------------------------------------
  * - All tensor pointers are DEVICE pointers owned by the caller.  The
  *   library allocates no memory (entry points that need scratch memory
- *   take a caller-owned workspace) and keeps no state besides a per-device
- *   cache of the architecture check and the compute-unit count; it is safe
- *   to call from several host threads.
+ *   take a caller-owned workspace; fa_fwd_bf16_decode_noalloc uses a static
+ *   device buffer instead) and keeps no state besides per-device caches of
+ *   the architecture check, the compute-unit count and that buffer's
+ *   address; it is safe to call from several host threads.
  * - Tensors are dense row-major ("contiguous").  Layout [B, H, N, d] means
  *   element (b, h, n, i) sits at ((b * H + h) * N + n) * d + i.
  * - Every pointer must be 16-byte aligned (FA_ERR_ALIGN otherwise).
@@ -45,7 +46,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 enum fa_status {
   FA_OK = 0,
@@ -56,7 +57,8 @@ enum fa_status {
   FA_ERR_ALIGN = -5,    /* a pointer is not 16-byte aligned                        */
   FA_ERR_DEVICE = -6,   /* no device, or the current device is not gfx950          */
   FA_ERR_LAUNCH = -7,   /* the kernel launch itself failed                         */
-  FA_ERR_WORKSPACE = -8 /* workspace missing or smaller than the split count needs */
+  FA_ERR_WORKSPACE = -8, /* workspace missing or smaller than the split count needs */
+  FA_ERR_SCRATCH = -9    /* the call needs more than the static scratch buffer holds  */
 };
 
 /* Flags of fa_fp8_prep. */
@@ -179,6 +181,33 @@ long long fa_fwd_bf16_decode_workspace(int B, int Hq, int Nq, int d, int splits)
 int fa_fwd_bf16_decode(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Hq, int Hkv,
                        int Nq, int Nk, int d, int causal, float softmax_scale, int num_splits, void* workspace,
                        long long workspace_bytes, void* stream);
+
+/*
+ * fa_fwd_bf16_decode_noalloc -- fa_fwd_bf16_decode for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It allocates nothing; the chunk partials
+ * go to a static device buffer of FA_DECODE_SCRATCH_BYTES (16 MiB) that the
+ * library holds on every device it runs on until the process ends.
+ *
+ *   q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, softmax_scale: as
+ *   fa_fwd_bf16_decode.
+ *   num_splits : >= 1 as fa_fwd_bf16_decode (FA_ERR_SCRATCH when that
+ *                count's partials, fa_fwd_bf16_decode_workspace bytes, exceed
+ *                the buffer), or 0 for the cost model's count on the current
+ *                device, lowered until the partials fit.
+ *
+ * The first call on a device looks the buffer up (hipGetSymbolAddress); make
+ * it outside graph capture.  Every call on a device shares that device's
+ * buffer and leaves its partials there: calls that overlap in time on one
+ * device (several streams or host threads) race and must be ordered by the
+ * caller.  The buffer needs no clearing: each chunk writes all of its
+ * partial rows before the merge reads them.  Results are bit-identical to
+ * fa_fwd_bf16_decode with the same effective split count.
+ */
+#define FA_DECODE_SCRATCH_BYTES (16ll << 20)
+int fa_fwd_bf16_decode_noalloc(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Hq,
+                               int Hkv, int Nq, int Nk, int d, int causal, float softmax_scale, int num_splits,
+                               void* stream);
 
 /*
  * fa_bwd_bf16 -- exact attention backward: dQ, dK, dV of the forward above

@@ -36,8 +36,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.fa_abi_version() == 1
-    for st in range(-8, 1):
+    assert lib.fa_abi_version() == 2
+    for st in range(-9, 1):
         assert lib.fa_status_string(st)
     assert lib.fa_fp8_vt_ld(1) == 128 and lib.fa_fp8_vt_ld(128) == 128 and lib.fa_fp8_vt_ld(129) == 256
     assert lib.fa_fp8_vt_ld(0) == 0
