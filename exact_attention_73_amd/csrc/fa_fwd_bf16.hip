@@ -500,6 +500,29 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, (min_blocks<D, VARLEN>())) voi
   }
 }
 
+// Causal workgroup order of the ping-pong kernel.  Workgroups reach the 8
+// XCDs round-robin by index, so XCD x runs workgroups x, x + 8, ...  Heads
+// are pinned to XCDs (x takes heads x, x + 8, ...) and each XCD walks its
+// heads four at a time, the heaviest query tiles first within each group of
+// four (heads alternating).  Against a global heavy-first order (every head
+// in flight on every XCD) this cuts the K/V bytes fetched from HBM from
+// 2.5-3.3 to 1.5-1.8 times the algorithmic bytes at N = 2048-4096, at equal
+// speed; walking one head at a time reaches 1.0 but leaves the heavy tiles
+// of each XCD's last head for the end (10-20 % slower).  Grids whose head
+// count does not split into such groups keep the global order.
+__device__ __forceinline__ void causal_order(int BH, int nq, int& bh, int& qt) {
+  constexpr int G = 4;
+  if ((BH & 7) == 0 && ((BH >> 3) % G) == 0) {
+    const int x = (int)blockIdx.x & 7, j = (int)blockIdx.x >> 3;
+    const int g = j / (G * nq), r = j - g * (G * nq);
+    qt = nq - 1 - r / G;
+    bh = x + 8 * (g * G + r % G);
+  } else {
+    qt = nq - 1 - (int)blockIdx.x / BH;
+    bh = (int)blockIdx.x % BH;
+  }
+}
+
 // d = 128 with an explicit ping-pong between two wave groups (FA3 explainer,
 // section "第二层重叠：Ping-Pong Scheduling"): eight waves per workgroup,
 // 32 query rows each; waves w and w + 4 share a SIMD.  The step of tile t is
@@ -510,7 +533,14 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, (min_blocks<D, VARLEN>())) voi
 // turns on the matrix core instead of contending for it.
 //   slot 2t:     group 0 matrix(t),  group 1 vector(t - 1)
 //   slot 2t + 1: group 0 vector(t),  group 1 matrix(t)
-// Stage t = {K_t, V_{t-1}} stays in LDS through slots 2t and 2t + 1.
+// Stage t = {K_t, V_{t-1}} stays in LDS through slots 2t and 2t + 1, in a
+// ring of three slots (96 KB at d = 128; with the 64 KB output staging the
+// workgroup takes the CU's whole 160 KB).  Each group issues half of a
+// stage's direct-to-LDS loads inside its vector part: issuing a stage's 32
+// one-KB loads stalls the issuing waves for about 300 cycles (the address
+// unit takes them one after another), which inside a matrix part idles the
+// matrix core and inside one vector part lengthens the other group's slot;
+// split over both vector parts it hides beside the other group's products.
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
   constexpr int BC = D == 256 ? 32 : 64, NW = 8, QW = 32, BR = NW * QW;
@@ -522,8 +552,10 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
 
   __shared__ __attribute__((aligned(1024))) uint16_t Ks0[BC * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Ks1[BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks2[BC * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Vs0[BC * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Vs1[BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs2[BC * D];
   // O is staged through LDS where a wave's fp32 tile fits a ring slot (d = 64, 128)
   constexpr bool kStageO = QW * D * 4 <= BC * D * 2;
   __shared__ __attribute__((aligned(1024))) float Ost[4][kStageO ? QW * D : 1];  // group 1's output staging
@@ -532,8 +564,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
   const int nq = (p.N + BR - 1) / BR;
   int bh, qt;
   if constexpr (CAUSAL) {
-    qt = nq - 1 - (int)blockIdx.x / BH;
-    bh = (int)blockIdx.x % BH;
+    causal_order(BH, nq, bh, qt);
   } else {
     const int w = xcd_contiguous((int)blockIdx.x, (int)gridDim.x);
     bh = w / nq;
@@ -720,31 +751,38 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
   // and group 1's in slot 2t + 1; stage t + 1 lands before slot 2t + 2, and
   // its ring slot last served stage t - 1, which group 1 finished in slot
   // 2t - 1.
+  // Stage s = {K_s, V_{s-1}} lives in ring slot s mod 3.  Each group
+  // requests half of stage t + 2 at the start of its vector part of stage
+  // t (group 0: K_{t+2} in slot 2t + 1, group 1: V_{t+1} in slot 2t + 2);
+  // that ring slot last held stage t - 1, which both groups finished in
+  // slots 2t - 2 and 2t - 1.  Group 0 waits for its half at the end of its
+  // vector part of stage t + 1, group 1 at the end of its matrix part of
+  // stage t + 1: both before the barrier that opens slot 2t + 4, where
+  // stage t + 2 is first read.  Requests past the last tile read zeros into
+  // a ring slot nobody reads again.
   auto stage = [&](int t, const uint16_t* kt, const uint16_t* vt, uint16_t* k_fill, uint16_t* v_fill)
                    __attribute__((always_inline)) {
-    if (grp == 0 && t >= 1) {  // stage 1 goes out with K_0 in the prologue
-      if (t + 1 < T) issue(rk, k_fill, koff, t + 1);
-      if (t < T) issue(rv, v_fill, voff, t);
-    }
     mfma_part(t, kt, vt);
-    // phase switch only: no memory is handed over here (the stage being read
-    // landed at the previous end-of-stage barrier, the vector part touches no
-    // LDS, and every K/V read of the matrix part is consumed by its product
-    // before the wave gets here), so no fence and no wait for the requests
-    // just issued
+    if (grp == 1) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): its half of stage t + 1
+    // phase switch: the only memory handed over is group 1's half of stage
+    // t + 1 (waited just above; the DMA writes LDS without the vector
+    // caches); the vector part touches no LDS and every K/V read of the
+    // matrix part is consumed by its product before the wave gets here, so
+    // no fence
     __builtin_amdgcn_s_barrier();
+    if (grp == 0) issue(rk, k_fill, koff, t + 2);
+    else issue(rv, v_fill, voff, t + 1);
     vector_part(t);
-    wait_vmem_all();
+    if (grp == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | IPL);  // all but this part's requests
     __syncthreads();
   };
 
-  // prologue: K_0, then stage 1 = {K_1, V_0}, requested whatever T is (past
-  // the keys the range check returns zeros; tiles past T land unused); wait
-  // for Q and K_0 only (the vector-memory counter drains in order)
+  // prologue: K_0, then stage 1 = {K_1, V_0}, by group 0 (past the keys the
+  // range check returns zeros); wait for Q and K_0 only
   if (grp == 0) {
     issue(rk, Ks0, koff, 0);
     issue(rk, Ks1, koff, 1);
-    issue(rv, Vs0, voff, 0);
+    issue(rv, Vs1, voff, 0);
     static_assert(2 * IPL <= 15, "the wait below encodes vmcnt in 4 bits");
     __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * IPL));  // vmcnt(stage 1's requests); expcnt, lgkmcnt left open
   } else {
@@ -755,14 +793,17 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
   // that the compiler may not move LDS accesses across
   asm volatile("s_barrier" ::: "memory");
   if (grp == 1) __syncthreads();  // group 1 sits out slot 0
-  // stage t: K_t in slot t mod 2, V_{t-1} in slot (t - 1) mod 2; stage 0
-  // peeled, so the loop is entered after its drain at the end of stage 0
-  stage(0, Ks0, Vs1, Ks1, Vs0);
-  for (int t = 1; t <= T; t += 2) {
-    stage(t, Ks1, Vs0, Ks0, Vs1);
-    if (t + 1 <= T) stage(t + 1, Ks0, Vs1, Ks1, Vs0);
+  // stage t reads K_t and V_{t-1} from ring slot t mod 3 and fills slot
+  // (t + 2) mod 3; stage 0 peeled
+  stage(0, Ks0, Vs0, Ks2, Vs2);
+  for (int t = 1; t <= T; t += 3) {
+    stage(t, Ks1, Vs1, Ks0, Vs0);
+    if (t + 1 <= T) stage(t + 1, Ks2, Vs2, Ks1, Vs1);
+    if (t + 2 <= T) stage(t + 2, Ks0, Vs0, Ks2, Vs2);
   }
   if (grp == 0) __syncthreads();  // group 0 sits out the last slot
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the last (unused) requests land before the ring is reused
+  __syncthreads();
 
   // epilogue: O / l, staged through LDS where it fits (group 0 in the ring,
   // group 1 in its own area) and stored as whole rows; every wave is past its
