@@ -81,4 +81,27 @@ __device__ __forceinline__ int xcd_contiguous(int bid, int n) {
   return (bid & 7) * (n >> 3) + (bid >> 3);
 }
 
+// Causal workgroup order of the ping-pong kernels (bf16 and FP8).  Workgroups reach the 8
+// XCDs round-robin by index, so XCD x runs workgroups x, x + 8, ...  Heads
+// are pinned to XCDs (x takes heads x, x + 8, ...) and each XCD walks its
+// heads four at a time, the heaviest query tiles first within each group of
+// four (heads alternating).  Against a global heavy-first order (every head
+// in flight on every XCD) this cuts the K/V bytes fetched from HBM from
+// 2.5-3.3 to 1.5-1.8 times the algorithmic bytes at N = 2048-4096, at equal
+// speed; walking one head at a time reaches 1.0 but leaves the heavy tiles
+// of each XCD's last head for the end (10-20 % slower).  Grids whose head
+// count does not split into such groups keep the global order.
+__device__ __forceinline__ void causal_order(int BH, int nq, int& bh, int& qt) {
+  constexpr int G = 4;
+  if ((BH & 7) == 0 && ((BH >> 3) % G) == 0) {
+    const int x = (int)blockIdx.x & 7, j = (int)blockIdx.x >> 3;
+    const int g = j / (G * nq), r = j - g * (G * nq);
+    qt = nq - 1 - r / G;
+    bh = x + 8 * (g * G + r % G);
+  } else {
+    qt = nq - 1 - (int)blockIdx.x / BH;
+    bh = (int)blockIdx.x % BH;
+  }
+}
+
 }  // namespace fa

@@ -556,8 +556,7 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_pp_kernel(FwdFp8Params p) {
   const int nb = (N + 127) / 128;  // scale blocks per head
   int bh, qt;
   if constexpr (CAUSAL) {
-    qt = nq - 1 - (int)blockIdx.x / BH;
-    bh = (int)blockIdx.x % BH;
+    causal_order(BH, nq, bh, qt);
   } else {
     const int w = xcd_contiguous((int)blockIdx.x, (int)gridDim.x);
     bh = w / nq;

@@ -70,15 +70,27 @@ constexpr float kLazyLog2 = 8.f;  // rescale only when a row max grows by more t
 // interleave on the matrix cores) beats two blocks per wave at one wave per
 // SIMD, which halves the LDS and L2 traffic per product but leaves a single
 // wave unable to hide its own latencies.
+//
+// DMA_IN_BLOCK: where a wave issues its share of the next tiles' direct-to-LDS
+// loads.  Issuing a step's loads back to back stalls the wave until the
+// address unit has taken them; at d = 256 (one wave per SIMD, nothing to
+// switch to) they go between the step's first products instead (same-box
+// A/B: +3.5 % at N = 2048, +7-9 % at N = 16384).  At d = 64 and 128 the step
+// keeps them ahead of its products: spread out they cost d = 64 spilled
+// registers and short d = 128 sequences the unconditional requests past the
+// last tile (-3 to -12 % at N <= 512).
 template <int D> struct Bf16Cfg;
 template <> struct Bf16Cfg<64> {
   static constexpr int QB = 1, NW = 4, BC = 64, MINB = 3;
+  static constexpr bool DMA_IN_BLOCK = false;
 };
 template <> struct Bf16Cfg<128> {
   static constexpr int QB = 1, NW = 4, BC = 64, MINB = 2;
+  static constexpr bool DMA_IN_BLOCK = false;
 };
 template <> struct Bf16Cfg<256> {
   static constexpr int QB = 1, NW = 4, BC = 32, MINB = 1;
+  static constexpr bool DMA_IN_BLOCK = true;
 };
 template <int D> constexpr int rows_per_workgroup() { return Bf16Cfg<D>::NW * 32 * Bf16Cfg<D>::QB; }
 // Workgroups per CU the register budget is cut for.  At d = 64 a wave issues
@@ -130,7 +142,9 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* src) {
 // row-max instructions of the next tile in between.  Values from a measured
 // sweep on MI355X (all within +-3 %; no hints at all loses 5 % causal).
 constexpr int kKLead = 2, kVLead = 4, kVPM = 3, kVPP = 2;
-template <int NKR, int NVR, int QB>
+// NDMA direct-to-LDS loads (when the step issues them in its block) go one
+// after each of the first NDMA K operand reads.
+template <int NKR, int NVR, int QB, int NDMA>
 __device__ __forceinline__ void schedule_step() {
   {
     __builtin_amdgcn_sched_group_barrier(0x100, kKLead, 0);
@@ -142,6 +156,7 @@ __device__ __forceinline__ void schedule_step() {
         __builtin_amdgcn_sched_group_barrier(0x002, kVPM, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < NDMA) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, kVLead, 0);
 #pragma unroll
@@ -346,10 +361,13 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, (min_blocks<D, VARLEN>())) voi
                   const uint16_t* k_next, const uint16_t* v_this, uint16_t* v_next) {
     wait_vmem_all();
     __syncthreads();  // V_j and K_{j+1} are in LDS; every wave is done with K_j and V_{j-1}
-    if (j + 2 < ntiles) issue(rk, k_this, koff, j + 2);
-    if (j + 1 < ntiles) issue(rv, v_next, voff, j + 1);
     const int key0 = j * BC;
-    if (CAUSAL && key0 > q0 + QW - 1 + off) return;  // every row of this wave lies above tile j (and all later ones)
+    const bool skip = CAUSAL && key0 > q0 + QW - 1 + off;  // every row of this wave lies above tile j (and later ones)
+    if (!Cfg::DMA_IN_BLOCK || skip) {
+      if (j + 2 < ntiles) issue(rk, k_this, koff, j + 2);
+      if (j + 1 < ntiles) issue(rv, v_next, voff, j + 1);
+    }
+    if (skip) return;
 
     // ---- mask (only tiles crossing the diagonal or the end of N) ----------
     const bool need_mask = (CAUSAL && key0 + BC - 1 > q0 + off) || (key0 + BC > Nk);
@@ -389,6 +407,13 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, (min_blocks<D, VARLEN>())) voi
     // while exp2 / bf16 cast / row sums of S_j run on the vector ALUs; then
     // O^T += V_j^T P_j^T while the row max of S_{j+1} is taken.  For the
     // last tile the first product reads a stale slot and is never used.
+    if constexpr (Cfg::DMA_IN_BLOCK) {
+      // this wave's share of K_{j+2} and V_{j+1}, spread between the products
+      // below (past the last tile the range check reads zeros into a slot
+      // that is not read again)
+      issue(rk, k_this, koff, j + 2);
+      issue(rv, v_next, voff, j + 1);
+    }
     qk(s_out, k_next);
     bf16x8 pb[QB][NPS];
 #pragma unroll
@@ -425,7 +450,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, (min_blocks<D, VARLEN>())) voi
       }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mx[qb] = rowmax(s_out[qb]);
-    schedule_step<NKB * NQS, NPS * NDB, QB>();
+    schedule_step<NKB * NQS, NPS * NDB, QB, Cfg::DMA_IN_BLOCK ? 2 * IPW : 0>();
   };
 
   // ---- prologue: K_0, V_0, K_1 in flight; S_0 and its row max ---------------
@@ -446,6 +471,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, (min_blocks<D, VARLEN>())) voi
     if (j + 1 < ntiles) step(j + 1, sb, sa, mx, Ks1, Ks0, Vs1, Vs0);
   }
 
+  if constexpr (Cfg::DMA_IN_BLOCK) wait_vmem_all();  // the last (unused) requests land before the ring is reused
   // ---- epilogue: O / l, lse = m * scale + ln l ----------------------------
   // A lane holds 16-byte pieces of ONE output row, so storing straight from
   // the accumulators writes 32 bytes into each of 32 rows per instruction.
@@ -497,29 +523,6 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, (min_blocks<D, VARLEN>())) voi
           }
       }
     }
-  }
-}
-
-// Causal workgroup order of the ping-pong kernel.  Workgroups reach the 8
-// XCDs round-robin by index, so XCD x runs workgroups x, x + 8, ...  Heads
-// are pinned to XCDs (x takes heads x, x + 8, ...) and each XCD walks its
-// heads four at a time, the heaviest query tiles first within each group of
-// four (heads alternating).  Against a global heavy-first order (every head
-// in flight on every XCD) this cuts the K/V bytes fetched from HBM from
-// 2.5-3.3 to 1.5-1.8 times the algorithmic bytes at N = 2048-4096, at equal
-// speed; walking one head at a time reaches 1.0 but leaves the heavy tiles
-// of each XCD's last head for the end (10-20 % slower).  Grids whose head
-// count does not split into such groups keep the global order.
-__device__ __forceinline__ void causal_order(int BH, int nq, int& bh, int& qt) {
-  constexpr int G = 4;
-  if ((BH & 7) == 0 && ((BH >> 3) % G) == 0) {
-    const int x = (int)blockIdx.x & 7, j = (int)blockIdx.x >> 3;
-    const int g = j / (G * nq), r = j - g * (G * nq);
-    qt = nq - 1 - r / G;
-    bh = x + 8 * (g * G + r % G);
-  } else {
-    qt = nq - 1 - (int)blockIdx.x / BH;
-    bh = (int)blockIdx.x % BH;
   }
 }
 
