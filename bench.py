@@ -34,7 +34,7 @@ profiles/fwd_bf16_N4096_noncausal_traffic.md together with the SHA-256 of
 the kernel's sources; it is null when those sources changed since.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
-                       [--legs std,sweep,sweep64,sweep256,long,fp8,bwd,decode,varlen] [--copy-calibration]
+                       [--legs std,sweep,sweep64,sweep256,long,fp8,bwd,decode,varlen,mfma_loop] [--copy-calibration]
 """
 
 from __future__ import annotations
@@ -58,7 +58,7 @@ TRAFFIC_SOURCES = ("exact_attention_73_amd/csrc/fa_fwd_bf16.hip", "exact_attenti
 COPY_CALIBRATION_BYTES = 256 << 20
 
 
-ALL_LEGS = ("std", "sweep", "sweep64", "sweep256", "long", "fp8", "bwd", "decode", "varlen")
+ALL_LEGS = ("std", "sweep", "sweep64", "sweep256", "long", "fp8", "bwd", "decode", "varlen", "mfma_loop")
 
 
 def fwd_bytes(B, H, N, d):
@@ -417,6 +417,9 @@ def main():
             "us": round(st["mean"] * 1e6, 1), "padded_to_longest_us": round(sp["mean"] * 1e6, 1)}
         del qv_, kv_, vv_, ov_, lv_, qp, kp, vp
 
+    if "mfma_loop" in legs_on:
+        legs["mfma_loop"] = mfma_loop_rates(torch, dev)
+
     if args.copy_calibration:
         src = torch.ones(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -451,6 +454,8 @@ def main():
             "device": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count,
             "torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
             "host_wall_s": round(wall, 4),
+            "mfma_loop_tflops": ({k_: legs["mfma_loop"][k_] for k_ in ("bf16", "fp8")}
+                                 if legs.get("mfma_loop") else None),
             "fp8": ({k_: legs["fp8"][k_] for k_ in ("workload", "fwd_fp8_tflops", "fwd_fp8_frac_of_fp8_peak",
                                                     "fwd_fp8_causal_tflops", "fwd_fp8_vpow2_tflops",
                                                     "prep_qk_rotated_gbps", "prep_v_transposed_gbps",
@@ -465,11 +470,52 @@ def main():
             "frac": round(achieved / PEAK_BF16, 4),
             "traffic": profiled_traffic(),
             "traffic_unit": "bytes per launch",
+            "frac_of_mfma_loop": (round(achieved / legs["mfma_loop"]["bf16"], 4) if legs.get("mfma_loop") else None),
         },
         "legs": legs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def mfma_loop_rates(torch, dev):
+    """Sustained matrix-core rate of this GPU in this run: one workgroup of 8
+    waves per CU, each wave issuing independent 32x32 products on register
+    operands (8 chains of bf16 32x32x16, 4 of FP8 32x32x64), timed with HIP
+    events; a reference point beside the published peaks.  Uses the test
+    probe library (tests/hip/libprobes.so) when it is built."""
+    import ctypes
+
+    path = os.path.join(ROOT, "tests", "hip", "libprobes.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.probe_mfma_rate.restype = ctypes.c_int
+    lib.probe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p]
+    grid = torch.cuda.get_device_properties(0).multi_processor_count
+    src = torch.full((512,), 0x3C003C00, dtype=torch.int32, device=dev)  # bf16 pairs of 1.0; E4M3 1.5 and 0
+    out = torch.empty(grid * 512, dtype=torch.float32, device=dev)
+    iters = 40000
+    res = {"workgroups": grid, "waves_per_simd": 2, "iters": iters}
+    for fp8, name, chains, flop in ((0, "bf16", 8, 2 * 32 * 32 * 16), (1, "fp8", 4, 2 * 32 * 32 * 64)):
+        st_ = torch.cuda.current_stream().cuda_stream
+        call = lambda: lib.probe_mfma_rate(fp8, src.data_ptr(), out.data_ptr(), iters, grid, st_)
+        ts = []
+        for i in range(7):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if call() != 0:
+                return None
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                ts.append(e0.elapsed_time(e1) / 1e3)
+        t = sorted(ts)[len(ts) // 2]
+        res[name] = round(grid * 8 * iters * chains * flop / t / 1e12, 1)
+    res["bf16_frac_of_published"] = round(res["bf16"] / PEAK_BF16, 4)
+    res["fp8_frac_of_published"] = round(res["fp8"] / PEAK_FP8, 4)
+    return res
 
 
 def cpu_baseline(B, H, N, d, seed):

@@ -553,12 +553,17 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
   constexpr int RPI = 1024 / ROWB;
   constexpr int NKB = BC / 32, NDB = D / 32, NQS = D / 16, NPS = BC / 16;
 
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks0[BC * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks1[BC * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks2[BC * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vs0[BC * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vs1[BC * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vs2[BC * D];
+  // The ring is one LDS array: a slot's address is then a constant offset of
+  // one base, which the reads' immediate offset field takes.  With one array
+  // per slot the compiler kept a separate set of per-lane read addresses for
+  // each slot (about 40 more VGPRs).
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[6 * BC * D];
+  uint16_t* const Ks0 = ring;
+  uint16_t* const Ks1 = ring + BC * D;
+  uint16_t* const Ks2 = ring + 2 * BC * D;
+  uint16_t* const Vs0 = ring + 3 * BC * D;
+  uint16_t* const Vs1 = ring + 4 * BC * D;
+  uint16_t* const Vs2 = ring + 5 * BC * D;
   // O is staged through LDS where a wave's fp32 tile fits a ring slot (d = 64, 128)
   constexpr bool kStageO = QW * D * 4 <= BC * D * 2;
   __shared__ __attribute__((aligned(1024))) float Ost[4][kStageO ? QW * D : 1];  // group 1's output staging
@@ -608,7 +613,8 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
   const int lastkey = q0 + QW - 1 + off;             // this wave's last visible key (causal)
   const int Tw = CAUSAL ? (lastkey < 0 ? 0 : min(T, lastkey / BC + 1)) : T;  // tiles this wave uses
 
-  // the four waves of group 0 load each stage (8 KB each); group 1 loads nothing
+  // tile requests: the four waves of a group each load a quarter of a K tile
+  // (group 0) or a V tile (group 1), 4 KB per wave and tile
   const int kvrowb = ex.kvstride * 2;
   const int kvbytes = Nk > 0 ? (Nk - 1) * kvrowb + ROWB : 0;
   const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(p.k + kvbase, kvbytes);

@@ -1,6 +1,8 @@
 // Test-only probes of gfx950 builtins whose lane layout or rounding the
 // attention kernels rely on.  Each probe runs one wave over a few KB of
-// caller-provided device buffers; every index stays inside them.
+// caller-provided device buffers; every index stays inside them.  One more,
+// probe_mfma_rate, measures the sustained matrix-core rate of the chip (a
+// reference point for the attention kernels' rates, not part of any test).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -81,7 +83,44 @@ __global__ void k_load_lds(const uint32_t* src, const int* off, int nbytes, uint
   for (int i = l; i < 320; i += 64) out[i] = lds[i];
 }
 
+// Sustained matrix-core rate: workgroups of 8 waves (2 per SIMD), each wave
+// issuing `iters` rounds of 8 (bf16, 32x32x16) or 4 (FP8 E4M3, 32x32x64,
+// unit block scales) independent products on register operands.  src: 512
+// ints of operand bits; out: one float per thread (keeps the products live).
+template <bool FP8>
+__global__ __launch_bounds__(512) void k_mfma_rate(const int* src, float* out, int iters) {
+  const int lane = threadIdx.x & 63;
+  f32x16 c[8] = {};
+  if constexpr (FP8) {
+    i32x8 a, b;
+    for (int j = 0; j < 8; ++j) {
+      a[j] = src[(8 * lane + j) & 255];
+      b[j] = src[256 + ((8 * lane + j) & 255)];
+    }
+    for (int i = 0; i < iters; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) c[k] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c[k], 0, 0, 0, 127, 0, 127);
+  } else {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const int4*>(src + 4 * (lane & 63)));
+    const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const int4*>(src + 256 + 4 * (lane & 63)));
+    for (int i = 0; i < iters; ++i)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) c[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[k], 0, 0, 0);
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) r += c[k][e];
+  out[blockIdx.x * 512 + threadIdx.x] = r;
+}
+
 extern "C" {
+int probe_mfma_rate(int fp8, const int* src, float* out, int iters, int grid, void* s) {
+  if (fp8) hipLaunchKernelGGL(k_mfma_rate<true>, dim3(grid), dim3(512), 0, (hipStream_t)s, src, out, iters);
+  else hipLaunchKernelGGL(k_mfma_rate<false>, dim3(grid), dim3(512), 0, (hipStream_t)s, src, out, iters);
+  return hipGetLastError();
+}
 int probe_load_lds(const uint32_t* src, const int* off, int nbytes, uint32_t* out, void* s) {
   hipLaunchKernelGGL(k_load_lds, dim3(1), dim3(64), 0, (hipStream_t)s, src, off, nbytes, out);
   return hipGetLastError();
