@@ -80,17 +80,19 @@ constexpr float kLazyLog2 = 8.f;  // rescale only when a row max grows by more t
 // registers and short d = 128 sequences the unconditional requests past the
 // last tile (-3 to -12 % at N <= 512).
 template <int D> struct Bf16Cfg;
+// ACC_IN_AGPR: the wave holds more than 256 registers, so the O accumulators
+// live in AGPRs (the matrix instructions read and write them there).
 template <> struct Bf16Cfg<64> {
   static constexpr int QB = 1, NW = 4, BC = 64, MINB = 3;
-  static constexpr bool DMA_IN_BLOCK = false;
+  static constexpr bool DMA_IN_BLOCK = false, ACC_IN_AGPR = false;
 };
 template <> struct Bf16Cfg<128> {
   static constexpr int QB = 1, NW = 4, BC = 64, MINB = 2;
-  static constexpr bool DMA_IN_BLOCK = false;
+  static constexpr bool DMA_IN_BLOCK = false, ACC_IN_AGPR = false;
 };
 template <> struct Bf16Cfg<256> {
   static constexpr int QB = 1, NW = 4, BC = 32, MINB = 1;
-  static constexpr bool DMA_IN_BLOCK = true;
+  static constexpr bool DMA_IN_BLOCK = true, ACC_IN_AGPR = true;
 };
 template <int D> constexpr int rows_per_workgroup() { return Bf16Cfg<D>::NW * 32 * Bf16Cfg<D>::QB; }
 // Workgroups per CU the register budget is cut for.  At d = 64 a wave issues
@@ -398,7 +400,17 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, (min_blocks<D, VARLEN>())) voi
         const float alpha = m_new == -INFINITY ? 1.f : exp2_fast((m_run[qb] - m_new) * c);
         l_run[qb] *= alpha;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) o[qb][db] *= alpha;
+        for (int db = 0; db < NDB; ++db) {
+          // With AGPR accumulators the operands of this (rare) multiply are
+          // pinned to AGPRs on both sides (empty asm, "a" constraint): the
+          // copy to vector registers and back then stays inside the branch.
+          // Left to itself the compiler kept a vector-register copy of all
+          // of O at the top of every step (128 AGPR reads per 32-key tile,
+          // about half the vector work of a d = 256 step).
+          if constexpr (Cfg::ACC_IN_AGPR) asm volatile("" : "+a"(o[qb][db]));
+          o[qb][db] *= alpha;
+          if constexpr (Cfg::ACC_IN_AGPR) asm volatile("" : "+a"(o[qb][db]));
+        }
         m_run[qb] = m_new;
       }
     }
