@@ -205,6 +205,7 @@ __global__ __launch_bounds__(DecCfg<D>::NW * 64, DecCfg<D>::MINB) void dec_bf16_
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
   const float c = p.c;
+  const float lazy = kLazyLog2 / c;  // the rescale threshold in raw score units
 
   auto step = [&](int i, uint16_t* slot) {
     wait_vmem<2 * LPT>();  // tile i has landed; only tile i + 1's loads may be outstanding
@@ -231,15 +232,28 @@ __global__ __launch_bounds__(DecCfg<D>::NW * 64, DecCfg<D>::MINB) void dec_bf16_
 #pragma unroll
     for (int rr = 0; rr < 16; rr += 2) mx = fmax3(mx, s[rr], s[rr + 1]);
     mx = max_halves(mx);
-    // online softmax update; a row that has seen no key yet keeps m = -inf,
-    // l = 0, O = 0 (and takes alpha = 1 rather than exp2(-inf - -inf))
-    const float m_new = __builtin_fmaxf(m_run, mx);
-    const float alpha = m_new == -INFINITY ? 1.f : exp2_fast((m_run - m_new) * c);
-    const float mc = m_new == -INFINITY ? 0.f : m_new * c;
-    m_run = m_new;
-    l_run *= alpha;
+    // online softmax update with the lazy reference of the prefill kernel:
+    // the exponent reference m moves only when some row of the wave has
+    // grown past it by more than kLazyLog2 (log2 units), so P <= 2^kLazyLog2
+    // and O, l are rescaled only on those tiles.  A row that has seen no key
+    // yet keeps m = -inf, l = 0, O = 0 (and takes alpha = 1 rather than
+    // exp2(-inf - -inf)).  Where O lives in AGPRs (more than 256 registers a
+    // wave) the multiply's operands are pinned to AGPRs on both sides (empty
+    // asm, "a" constraint), which keeps the copy to vector registers inside
+    // this rare branch.
+    if (__any(mx > m_run + lazy)) {
+      const float m_new = __builtin_fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : exp2_fast((m_run - m_new) * c);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+      for (int db = 0; db < NDB; ++db) {
+        if constexpr (D >= 128) asm volatile("" : "+a"(o[db]));
+        o[db] *= alpha;
+        if constexpr (D >= 128) asm volatile("" : "+a"(o[db]));
+      }
+    }
+    const float mc = m_run == -INFINITY ? 0.f : m_run * c;
     // P^T (bf16) as B operands: k-step ks covers keys 16 ks + 4 hi + 0..3 and
     // 16 ks + 8 + 4 hi + 0..3, registers 8 ks .. 8 ks + 7
     bf16x8 pb[2];

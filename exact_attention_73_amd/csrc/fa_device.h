@@ -29,6 +29,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Lazy rescale of the online softmax (bf16 forward and decode): the exponent
+// reference of a row moves only when its max grows by more than this many
+// log2 units, so P <= 2^kLazyLog2 and O, l are rescaled only then.
+constexpr float kLazyLog2 = 8.f;
 
 __device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

@@ -62,8 +62,6 @@
 namespace fa {
 namespace {
 
-constexpr float kLazyLog2 = 8.f;  // rescale only when a row max grows by more than 2^8
-
 // Per head size: QB 32-row query blocks per wave, NW waves per workgroup,
 // BC keys per tile, MINB workgroups per CU.  Measured on MI355X: one query
 // block per wave with two workgroups per CU (two waves per SIMD that
