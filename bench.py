@@ -513,6 +513,24 @@ def mfma_loop_rates(torch, dev):
                 ts.append(e0.elapsed_time(e1) / 1e3)
         t = sorted(ts)[len(ts) // 2]
         res[name] = round(grid * 8 * iters * chains * flop / t / 1e12, 1)
+    # LDS read rate per CU (bytes per ns): ds_read_b128 and the transposed
+    # ds_read_b64_tr_b16 of the forward's V operand
+    lib.probe_lds_rate.restype = ctypes.c_int
+    lib.probe_lds_rate.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    for tr, name, by in ((0, "lds_read_b128_bytes_per_ns_per_cu", 1024), (1, "lds_read_tr_b16_bytes_per_ns_per_cu", 512)):
+        st_ = torch.cuda.current_stream().cuda_stream
+        ts = []
+        for i in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if lib.probe_lds_rate(tr, out.data_ptr(), 20000, grid, st_) != 0:
+                return None
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 1:
+                ts.append(e0.elapsed_time(e1) / 1e3)
+        t = sorted(ts)[len(ts) // 2]
+        res[name] = round(8 * 20000 * 16 * by / t / 1e9, 1)
     res["bf16_frac_of_published"] = round(res["bf16"] / PEAK_BF16, 4)
     res["fp8_frac_of_published"] = round(res["fp8"] / PEAK_FP8, 4)
     return res

@@ -115,7 +115,45 @@ __global__ __launch_bounds__(512) void k_mfma_rate(const int* src, float* out, i
   out[blockIdx.x * 512 + threadIdx.x] = r;
 }
 
+// LDS read rate: workgroups of 8 waves, each wave issuing `iters` rounds of
+// 16 reads from the first 64 KB of an LDS array: ds_read_b128 (1 KB per wave-instruction,
+// consecutive 16 bytes per lane) or ds_read_b64_tr_b16 (512 bytes, the
+// transposed V read of the forward kernel: 128-element rows, chunk index
+// XOR (row & 3) << 2).  Every address stays inside the array.
+typedef __attribute__((address_space(3))) i16x4* lds_i16x4_t;
+template <bool TR>
+__global__ __launch_bounds__(512) void k_lds_rate(float* out, int iters) {
+  // 96 KB so that a CU holds one workgroup (the reads use the first 64 KB)
+  __shared__ __attribute__((aligned(1024))) float lds[24576];
+  for (int i = threadIdx.x; i < 16384; i += 512) lds[i] = 1e-3f * (i & 1023);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, grpv = lane >> 4, sl = lane & 15;
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  i16x4 acc2 = {0, 0, 0, 0};
+  for (int it = 0; it < iters; ++it) {
+    const int sh = (it & 3) * 1024;  // floats; a new address every round
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if constexpr (!TR) {
+        const float4 x = *reinterpret_cast<const float4*>(&lds[((wave * 16 + r) & 15) * 256 + sh + lane * 4]);
+        acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+      } else {
+        const int row = (r & 3) * 16 + 4 * (wave & 1) + (sl >> 2);
+        const int col = 32 * (r >> 2) + 16 * (grpv & 1) + 4 * (sl & 3);
+        const int e = row * 128 + (((col >> 3) ^ ((row & 3) << 2)) << 3) + (col & 7) + 2 * sh;  // < 32768
+        acc2 += __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t)(reinterpret_cast<const short*>(lds) + e));
+      }
+    }
+  }
+  out[blockIdx.x * 512 + threadIdx.x] = acc.x + acc.y + acc.z + acc.w + (float)(acc2[0] + acc2[1] + acc2[2] + acc2[3]);
+}
+
 extern "C" {
+int probe_lds_rate(int tr, float* out, int iters, int grid, void* s) {
+  if (tr) hipLaunchKernelGGL(k_lds_rate<true>, dim3(grid), dim3(512), 0, (hipStream_t)s, out, iters);
+  else hipLaunchKernelGGL(k_lds_rate<false>, dim3(grid), dim3(512), 0, (hipStream_t)s, out, iters);
+  return hipGetLastError();
+}
 int probe_mfma_rate(int fp8, const int* src, float* out, int iters, int grid, void* s) {
   if (fp8) hipLaunchKernelGGL(k_mfma_rate<true>, dim3(grid), dim3(512), 0, (hipStream_t)s, src, out, iters);
   else hipLaunchKernelGGL(k_mfma_rate<false>, dim3(grid), dim3(512), 0, (hipStream_t)s, src, out, iters);
