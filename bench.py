@@ -344,7 +344,7 @@ def main():
         # backward: 2.5 x the forward's FLOPs (dQ, dK, dV and the recomputed
         # S), halved for causal; the delta, dK/dV and dQ kernels in one call
         bw = {}
-        for (Bb, Hb, Nb, db) in ((4, 16, 2048, 128), (4, 16, 4096, 128), (4, 16, 2048, 64)):
+        for (Bb, Hb, Nb, db) in ((4, 16, 2048, 128), (4, 16, 4096, 128), (4, 16, 2048, 64), (4, 8, 2048, 256)):
             qb_, kb_, vb_ = (x.to(dev) for x in make_qkv(Bb, Hb, Nb, db, 73002))
             gb_ = make_do(Bb, Hb, Nb, db, 73002).to(dev)
             for causal in (False, True):

@@ -309,11 +309,11 @@ int bwd_common(const void* q, const void* k, const void* v, const float* o, cons
                float* dq, float* dk, float* dv, float* delta_ws, int B, int H, int Hkv, int N, int d, int causal,
                float softmax_scale, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta_ws) return FA_ERR_NULL_PTR;
-  if (int e = check_shape(B, H, N, d == 64 || d == 128 ? d : 1)) return e;
+  if (int e = check_shape(B, H, N, d == 64 || d == 128 || d == 256 ? d : 1)) return e;
   if (Hkv < 1 || H % Hkv) return FA_ERR_SHAPE;
   // fp32 [N, d] slices are addressed with 32-bit byte offsets too
   if ((double)N * (double)d * 4.0 >= 2147483648.0) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_HEADDIM;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   if (int e = check_scale(softmax_scale)) return e;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(dout) ||

@@ -34,10 +34,12 @@
 //    dK^T products, 32-query tiles): each fits 256 registers, so two waves
 //    share every SIMD, which outweighs computing S twice.  The arithmetic
 //    and its order are those of the single kernel, so results are the same
-//    bit for bit.
+//    bit for bit.  At d = 256 the dK/dV work always runs as the two launches
+//    (one wave per SIMD each; a single wave holding K, V and both 256-wide
+//    accumulators would spill hundreds of registers).
 //  * bwd_dq_kernel: shaped like the forward: one workgroup per 128 queries,
-//    Q and dO resident as B operands, K and V tiles of 64 keys through the
-//    LDS ring; S^T = K Q^T, dP^T = V dO^T (a lane owns one query, so lse and
+//    Q and dO resident as B operands, K and V tiles of 64 keys (32 at
+//    d = 256) through the LDS ring; S^T = K Q^T, dP^T = V dO^T (a lane owns one query, so lse and
 //    D are per-lane scalars) and dQ^T += K^T dS^T from transposed K reads.
 // Causal: key tiles above a query tile (or query tiles before a key tile)
 // are skipped; only tiles crossing the diagonal are masked element-wise.
@@ -150,9 +152,16 @@ enum DkdvPart { kBoth = 0, kDvOnly = 1, kDkOnly = 2 };
 
 template <int D> struct BwdCfg {
   static constexpr int kDkdvMinb = D == 64 ? 2 : 1;  // both gradients in one wave
-  static constexpr int kDqMinb = 2;
+  // d = 256: Q and dO rows (128 registers) and the dQ accumulators (128)
+  // leave a dQ wave more than 256 registers
+  static constexpr int kDqMinb = D == 256 ? 1 : 2;
 };
-template <int D, int PART> constexpr int dkdv_minb() { return PART == kBoth ? BwdCfg<D>::kDkdvMinb : 2; }
+// the split launches fit two waves per SIMD at d = 128; at d = 256 a
+// workgroup's 64 KB (dK) or 128 KB (dV) of tiles and its registers (K and V
+// rows plus one accumulator: 256) allow one per CU
+template <int D, int PART> constexpr int dkdv_minb() {
+  return PART == kBoth ? BwdCfg<D>::kDkdvMinb : (D == 256 ? 1 : 2);
+}
 template <int PART> constexpr int dkdv_bq() { return PART == kDkOnly ? 32 : 64; }
 
 template <int D, bool CAUSAL, int PART>
@@ -306,11 +315,27 @@ __global__ __launch_bounds__(kBwdThreads, (dkdv_minb<D, PART>())) void bwd_dkdv_
     }
   };
 
+  // Where a wave holds more than 256 registers its dK, dV accumulators live
+  // in AGPRs; pinning them there at the loop's top and bottom (empty asm,
+  // "a" constraint) stops the compiler from keeping vector-register copies
+  // of them that it refreshes every iteration (about 300 AGPR moves per two
+  // query tiles at d = 256 before, the 64 reads of S and dP after)
+  auto pin = [&]() __attribute__((always_inline)) {
+    if constexpr (D == 256 || (D == 128 && PART == kBoth)) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        if constexpr (DO_V) asm volatile("" : "+a"(dv[db]));
+        if constexpr (DO_K) asm volatile("" : "+a"(dk[db]));
+      }
+    }
+  };
   if (ntl > 0) {
     issue(Qs0, Gs0, Ls0, Ds0, 0);
     for (int t = 0; t < ntl; t += 2) {
+      pin();
       step(t, Qs0, Gs0, Ls0, Ds0, Qs1, Gs1, Ls1, Ds1);
       if (t + 1 < ntl) step(t + 1, Qs1, Gs1, Ls1, Ds1, Qs0, Gs0, Ls0, Ds0);
+      pin();
     }
   }
 
@@ -336,7 +361,7 @@ __global__ __launch_bounds__(kBwdThreads, (dkdv_minb<D, PART>())) void bwd_dkdv_
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, BwdCfg<D>::kDqMinb) void bwd_dq_kernel(BwdBf16Params p) {
-  constexpr int BC = 64;             // keys per tile
+  constexpr int BC = D == 256 ? 32 : 64;  // keys per tile (d = 256: two 16 KB tiles per slot)
   constexpr int NKB = BC / 32;
   constexpr int NQS = D / 16;
   constexpr int NDB = D / 32;
@@ -451,8 +476,17 @@ __global__ __launch_bounds__(kBwdThreads, BwdCfg<D>::kDqMinb) void bwd_dq_kernel
 
   issue(Ks0, Vs0, 0);
   for (int j = 0; j < ntiles; j += 2) {
+    // dQ accumulators in AGPRs at d = 256: pinned as in the dK/dV kernel
+    if constexpr (D == 256) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) asm volatile("" : "+a"(dq[db]));
+    }
     step(j, Ks0, Vs0, Ks1, Vs1);
     if (j + 1 < ntiles) step(j + 1, Ks1, Vs1, Ks0, Vs0);
+    if constexpr (D == 256) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) asm volatile("" : "+a"(dq[db]));
+    }
   }
 
   if (qok) {
@@ -476,15 +510,22 @@ hipError_t launch(const BwdBf16Params& p, hipStream_t stream) {
   const unsigned bh = (unsigned)p.B * (unsigned)p.H;    // dQ: one workgroup per query head's 128 rows
   const unsigned bk = (unsigned)p.B * (unsigned)p.Hkv;  // dK/dV: one per KV head's 128 keys
   const unsigned tiles = (unsigned)((p.N + 127) / 128);
-  bool split = false;
-  if constexpr (D == 128) {
-    if (p.split_dkdv) {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kDvOnly>), dim3(bk * tiles), dim3(kBwdThreads), 0, stream, p);
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kDkOnly>), dim3(bk * tiles), dim3(kBwdThreads), 0, stream, p);
-      split = true;
+  // d = 256 always splits: one wave holding K, V and both accumulators
+  // (512 registers of state) spills hundreds of registers
+  if constexpr (D == 256) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kDvOnly>), dim3(bk * tiles), dim3(kBwdThreads), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kDkOnly>), dim3(bk * tiles), dim3(kBwdThreads), 0, stream, p);
+  } else {
+    bool split = false;
+    if constexpr (D == 128) {
+      if (p.split_dkdv) {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kDvOnly>), dim3(bk * tiles), dim3(kBwdThreads), 0, stream, p);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kDkOnly>), dim3(bk * tiles), dim3(kBwdThreads), 0, stream, p);
+        split = true;
+      }
     }
+    if (!split) hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kBoth>), dim3(bk * tiles), dim3(kBwdThreads), 0, stream, p);
   }
-  if (!split) hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kBoth>), dim3(bk * tiles), dim3(kBwdThreads), 0, stream, p);
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(bh * tiles), dim3(kBwdThreads), 0, stream, p);
   return hipGetLastError();
 }
@@ -495,6 +536,7 @@ hipError_t launch_bwd_bf16(const BwdBf16Params& p, int d, bool causal, hipStream
   switch (d) {
     case 64: return causal ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
     case 128: return causal ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
+    case 256: return causal ? launch<256, true>(p, stream) : launch<256, false>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

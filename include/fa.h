@@ -224,11 +224,13 @@ int fa_fwd_bf16_decode_noalloc(const void* q, const void* k, const void* v, floa
  *   dq, dk, dv    : fp32 [B, H, N, d]   (every element written)
  *   delta_ws      : fp32 [B, H, N]      caller-owned workspace, overwritten
  *                                       with D (the library allocates nothing)
- *   d             : 64 or 128           (FA_ERR_HEADDIM otherwise)
+ *   d             : 64, 128 or 256      (FA_ERR_HEADDIM otherwise)
  *   causal, softmax_scale : as for the forward, and equal to its values.
  *
- * Also FA_ERR_SHAPE when N * d * 4 >= 2^31.  Three kernels run in order on
- * `stream`: D, then dK/dV, then dQ; no atomics, so results are deterministic.
+ * Also FA_ERR_SHAPE when N * d * 4 >= 2^31.  The kernels run in order on
+ * `stream`: D, then dK/dV (one launch, or a dV launch and a dK launch: always
+ * at d = 256, at d = 128 when the grid fills the device), then dQ; no
+ * atomics, so results are deterministic.
  */
 int fa_bwd_bf16(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
                 float* dq, float* dk, float* dv, float* delta_ws, int B, int H, int N, int d, int causal,

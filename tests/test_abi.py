@@ -127,8 +127,8 @@ def test_bwd_validation(lib):
                                      kw.get("ws", FAKE), kw.get("B", 1), 1, kw.get("N", 64), kw.get("d", 128),
                                      kw.get("causal", 0), kw.get("scale", 0.1), None)
     assert f(q=None) == -1 and f(ws=None) == -1
-    assert f(B=0) == -2 and f(N=1 << 22) == -2  # N * d * 4 >= 2^31
-    assert f(d=256) == -3 and f(d=32) == -3
+    assert f(B=0) == -2 and f(N=1 << 22) == -2 and f(N=1 << 21, d=256) == -2  # N * d * 4 >= 2^31
+    assert f(d=96) == -3 and f(d=32) == -3
     assert f(causal=3) == -4 and f(scale=0.0) == -4
     assert f(ws=FAKE + 4) == -5
 
@@ -138,7 +138,7 @@ def test_bwd_gqa_validation(lib):
                                          kw.get("Hq", 8), kw.get("Hkv", 2), 64, kw.get("d", 128), 0, 0.1, None)
     assert f(q=None) == -1
     assert f(Hkv=0) == -2 and f(Hq=6, Hkv=4) == -2 and f(Hq=0) == -2
-    assert f(d=256) == -3
+    assert f(d=96) == -3
 
 
 def test_valid_call_without_gpu_reports_device_error(lib):

@@ -31,14 +31,20 @@ def _check(got, ref, label):
     for name, g, r in zip(("dq", "dk", "dv"), got, ref):
         assert np.isfinite(g).all(), (label, name)
         e = errors(g, r)
-        big = float(np.abs(r).max()) or 1.0
+        big = float(np.abs(r).max())
         print(f"{label} {name}: {e}")
+        if big == 0.0:
+            # an exactly zero gradient (one visible key: softmax 1, so dS = P (dP - D) = 0):
+            # the GPU forms dP with the matrix cores and D = rowsum(dO * O) in another
+            # fp32 order, so dS keeps residues of fp32 rounding (2^-24 of |dP|)
+            assert e["max_abs"] <= 1e-5, (label, name, e)
+            continue
         assert e["rel_rmse"] <= 1e-2, (label, name, e)
         assert e["max_abs"] <= 2e-2 * big, (label, name, e)
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("N", [1, 17, 64, 65, 127, 128, 129, 200, 255, 300])
 def test_bwd_edges(N, d, causal):
     q, k, v = make_qkv(1, 2, N, d, seed=6000 + N + d)
@@ -49,12 +55,13 @@ def test_bwd_edges(N, d, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_bwd_multi_tile(causal):
-    q, k, v = make_qkv(2, 4, 1000, 128, seed=6100)
-    do = make_do(2, 4, 1000, 128, seed=6100)
+@pytest.mark.parametrize("d", [128, 256])
+def test_bwd_multi_tile(causal, d):
+    q, k, v = make_qkv(2, 4, 1000, d, seed=6100)
+    do = make_do(2, 4, 1000, d, seed=6100)
     got = _run(q, k, v, do, causal)
-    ref = attention_bwd_ref(q, k, v, do, causal=causal, scale=softmax_scale(128))
-    _check(got, ref, f"B2 H4 N1000 causal={causal}")
+    ref = attention_bwd_ref(q, k, v, do, causal=causal, scale=softmax_scale(d))
+    _check(got, ref, f"B2 H4 N1000 d={d} causal={causal}")
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -97,7 +104,7 @@ def _gqa_inputs(B, Hq, Hkv, N, d, seed):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,Hq,Hkv,N,d", [(1, 4, 2, 300, 128), (1, 6, 1, 129, 64), (2, 8, 2, 1000, 128),
-                                           (1, 4, 4, 200, 64), (1, 8, 1, 64, 128)])
+                                           (1, 4, 4, 200, 64), (1, 8, 1, 64, 128), (1, 4, 2, 300, 256)])
 def test_bwd_gqa_against_oracle(B, Hq, Hkv, N, d, causal):
     q, k, v, do = _gqa_inputs(B, Hq, Hkv, N, d, seed=6400 + N + d + Hq)
     qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
@@ -159,8 +166,8 @@ def test_bwd_deterministic():
 
 
 def test_bwd_invalid_arguments():
-    q, k, v = (x.cuda() for x in make_qkv(1, 1, 64, 256, seed=1))
-    o = torch.zeros(1, 1, 64, 256, device="cuda")
+    q, k, v = (x.cuda() for x in make_qkv(1, 1, 64, 96, seed=1))
+    o = torch.zeros(1, 1, 64, 96, device="cuda")
     lse = torch.zeros(1, 1, 64, device="cuda")
     with pytest.raises(fa.FaError) as ei:
         fa.bwd_bf16(q, k, v, o, lse, q)
