@@ -12,7 +12,9 @@ from exact_attention_73_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
-FAKE = 0x10000  # aligned, never dereferenced (validation fails first)
+# aligned, never dereferenced: every call below fails some validation step,
+# so none launches even where a GPU is present
+FAKE = 0x10000
 
 
 def _declared():
@@ -41,6 +43,16 @@ def test_version_and_strings(lib):
         assert lib.fa_status_string(st)
     assert lib.fa_fp8_vt_ld(1) == 128 and lib.fa_fp8_vt_ld(128) == 128 and lib.fa_fp8_vt_ld(129) == 256
     assert lib.fa_fp8_vt_ld(0) == 0
+
+
+def test_fp8_ref_block(lib):
+    """The FP8 forward's exponent-reference block: the key tile of the kernel
+    it runs (128-key tiles for long sequences, 64 otherwise), host only."""
+    f = lib.fa_fp8_ref_block
+    assert [f(N, 0) for N in (1, 64, 1023, 1024, 4096, 1 << 20)] == [64, 64, 64, 128, 128, 128]
+    assert [f(N, 1) for N in (1, 1024, 4095, 4096, 16384)] == [64, 64, 64, 128, 128]
+    assert f(0, 0) == -2 and f(-5, 1) == -2 and f(64, 2) == -4
+    assert all(128 % f(N, c) == 0 for N in (1, 100, 5000) for c in (0, 1))  # divides the scale block
 
 
 def _bf16(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, l=FAKE, B=1, H=1, N=16, d=128, causal=0, scale=0.125):
@@ -119,7 +131,9 @@ def test_decode_validation(lib):
     assert f(d=32) == -3 and f(causal=2) == -4 and f(splits=0) == -4
     need = 4 * 8 * 129 * 4
     assert f(ws=None) == -8 and f(wsb=need - 1) == -8 and f(ws=FAKE + 4, wsb=need) == -5
-    assert f(ws=None, splits=1) != -8  # one chunk needs no workspace
+    # one chunk needs no workspace: the call gets past that check to the
+    # alignment one (a fully valid call would launch on the fake pointers)
+    assert f(ws=None, splits=1, q=FAKE + 8) == -5
 
 
 def test_bwd_validation(lib):
