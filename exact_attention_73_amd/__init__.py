@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     decode_workspace_bytes,
     fp8_prep,
     fp8_prep_v,
+    fp8_ref_block,
     fp8_vt_ld,
     fwd_bf16,
     fwd_bf16_decode,
@@ -24,4 +25,4 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["fwd_bf16", "fwd_bf16_gqa", "fwd_bf16_varlen", "fwd_bf16_decode", "fwd_bf16_decode_noalloc", "decode_splits", "decode_workspace_bytes",
-           "bwd_bf16", "bwd_bf16_gqa", "fp8_prep", "fp8_prep_v", "fwd_fp8", "fp8_vt_ld", "load", "FaError"]
+           "bwd_bf16", "bwd_bf16_gqa", "fp8_prep", "fp8_prep_v", "fwd_fp8", "fp8_vt_ld", "fp8_ref_block", "load", "FaError"]

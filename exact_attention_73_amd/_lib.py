@@ -35,6 +35,7 @@ SIGNATURES = {
     "fa_bwd_bf16": (_I, [_VP, _VP, _VP, _FP, _FP, _VP, _FP, _FP, _FP, _FP, _I, _I, _I, _I, _I, _F, _VP]),
     "fa_fp8_prep": (_I, [_VP, _VP, _FP, _VP, _I, _I, _I, _I, ctypes.c_uint, _VP]),
     "fa_fp8_vt_ld": (_I, [_I]),
+    "fa_fp8_ref_block": (_I, [_I, _I]),
     "fa_fwd_fp8": (_I, [_VP, _VP, _VP, _FP, _FP, _FP, _FP, _FP, _I, _I, _I, _I, _I, _F, _VP]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_abi_version": (_I, []),
@@ -110,6 +111,13 @@ def fwd_bf16(q, k, v, causal: bool = False, softmax_scale: float | None = None, 
 
 def fp8_vt_ld(N: int) -> int:
     return int(load().fa_fp8_vt_ld(int(N)))
+
+
+def fp8_ref_block(N: int, causal: bool = False) -> int:
+    """Keys per exponent-reference step of :func:`fwd_fp8` for ``N`` keys."""
+    r = int(load().fa_fp8_ref_block(int(N), int(bool(causal))))
+    _check("fa_fp8_ref_block", r if r < 0 else 0)
+    return r
 
 
 def fwd_bf16_gqa(q, k, v, causal: bool = False, softmax_scale: float | None = None, out=None, lse=None):

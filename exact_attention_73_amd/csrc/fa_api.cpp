@@ -120,6 +120,12 @@ const char* fa_status_string(int status) {
 
 int fa_fp8_vt_ld(int N) { return N < 1 ? 0 : ((N + 127) / 128) * 128; }
 
+int fa_fp8_ref_block(int N, int causal) {
+  if (N < 1) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  return fa::fwd_fp8_ref_block(N, causal == 1);
+}
+
 int fa_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int N, int d,
                 int causal, float softmax_scale, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_PTR;

@@ -262,6 +262,7 @@ constexpr int kWaves = 4;
 constexpr int kQW = 32;
 constexpr int kBR = kWaves * kQW;  // 128 = one scale block of queries
 constexpr int kBC = 64;            // keys per tile (half a scale block)
+constexpr int kPPKeys = 128;       // keys per tile of the ping-pong kernel (one scale block)
 constexpr int kThreads = kWaves * 64;
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
@@ -280,7 +281,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 }
 
 // 16-byte chunk swizzles: K rows are 128 bytes (two rows per 256 bytes of
-// banks), V^T tile rows are 64 bytes (four rows per 256 bytes).
+// banks), V^T tile rows are 64 bytes (four rows per 256 bytes); the
+// ping-pong kernel's 128-key V^T tile rows are 128 bytes and take the K one.
 __device__ __forceinline__ int k8_swizzle(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int v8_swizzle(int d) { return (d >> 2) & 3; }
 
@@ -435,13 +437,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
 
     const bool need_mask = (CAUSAL && key0 + kBC - 1 > q0) || (key0 + kBC > N);
     if (need_mask) {
+      // key = key0 + 4 hi + off, off a constant per register: the key is past
+      // the row (causal) or past N iff off > lim
+      int lim = N - 1 - key0 - 4 * hi;
+      if constexpr (CAUSAL) lim = min(lim, qrow - key0 - 4 * hi);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool dead = (CAUSAL && key > qrow) || key >= N;
-          s_in[kb][r] = dead ? -INFINITY : s_in[kb][r];
+          const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+          s_in[kb][r] = off > lim ? -INFINITY : s_in[kb][r];
         }
       mx = rowmax(s_in);
     }
@@ -453,7 +458,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
 
     qk(s_out, k_next);  // S_{j+1}: matrix cores, while the exps below run
     i32x8 pb;
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+    float ls[4] = {-0.f, -0.f, -0.f, -0.f};  // x + -0 = x: the first adds fold away
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const int kb = w >> 2, r = 4 * (w & 3);
@@ -531,19 +536,27 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
 // FP8 forward with the matrix/vector ping-pong of the bf16 d = 128 kernel
 // (FA3 explainer, section "第二层重叠：Ping-Pong Scheduling"): eight waves per
 // workgroup (256 query rows, two 128-row Q scale blocks), waves w and w + 4
-// on one SIMD.  A tile's step splits into a matrix part (S_t = K_t Q^T: 4
-// products; O^T += V_{t-1}^T P_{t-1}^T: 4 products with the per-lane E8M0
-// scales) and a vector part (the FP8 softmax of S_t: mask, power-of-two
-// exponent reference, E4M3 P, fp32 row sum, rare rebase).  In every slot one
-// group runs matrix parts while the other runs vector parts; group 1 runs
-// the same sequence one slot later.  Stage t = {K_t, V_{t-1}^T} (16 KB) is
-// requested by group 0 at the start of its matrix part of stage t - 1.
+// on one SIMD.  Its tiles are 128 keys, one K and V scale block each (the
+// four-wave kernel's are 64): an FP8 product does the work of four bf16 ones
+// in twice the cycles, so 128-key tiles give each slot as many matrix cycles
+// as the bf16 kernel's 64-key slots and halve the barriers per key (measured
+// 1.06-1.10 x over 64-key tiles).  The exponent reference therefore moves
+// once per 128 keys (fa_fp8_ref_block).  A tile's step splits into a matrix
+// part (S_t = K_t Q^T: 8 products; O^T += V_{t-1}^T P_{t-1}^T: 8 products with
+// the per-lane E8M0 scales, two per 32 rows of d, one per 64-key half) and a
+// vector part (the FP8 softmax of S_t: mask, power-of-two exponent
+// reference, E4M3 P, fp32 row sum, rare rebase).  In every slot one group
+// runs matrix parts while the other runs vector parts; group 1 runs the same
+// sequence one slot later.  Stage t = {K_t, V_{t-1}^T} (32 KB) is requested
+// by group 0 at the start of its matrix part of stage t - 1.
 template <bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void fwd_fp8_pp_kernel(FwdFp8Params p) {
   constexpr int D = 128, NW = 8, BR = NW * kQW;
-  constexpr int NKB = kBC / 32, NDB = D / 32, NQS = D / 64;
-  constexpr int TILE = kBC * D;          // bytes of a K tile (and of a V^T tile)
+  constexpr int KT = kPPKeys;            // keys per tile
+  constexpr int NKB = KT / 32, NDB = D / 32, NQS = D / 64, NSUB = KT / 64;
+  constexpr int TILE = KT * D;           // bytes of a K tile (and of a V^T tile)
   constexpr int IPL = TILE / 1024 / 4;   // 1 KB wave-loads per loading wave and tile
+  constexpr int CPR = KT / 16;           // 16-byte chunks per V^T tile row
 
   __shared__ __attribute__((aligned(1024))) uint8_t Ks0[TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t Ks1[TILE];
@@ -589,10 +602,11 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_pp_kernel(FwdFp8Params p) {
   }
 
   const int kend = CAUSAL ? min(N, qt * BR + BR) : N;
-  const int T = (kend + kBC - 1) / kBC;                                   // tiles of the workgroup
-  const int Tw = CAUSAL ? min(T, (q0 + kQW - 1) / kBC + 1) : T;           // tiles this wave uses
+  const int T = (kend + KT - 1) / KT;                                     // tiles of the workgroup
+  const int Tw = CAUSAL ? min(T, (q0 + kQW - 1) / KT + 1) : T;            // tiles this wave uses
 
-  // group 0 loads each stage: K rows of 128 bytes, V^T rows of 64 bytes
+  // group 0 loads each stage: K rows and V^T tile rows of 128 bytes, with
+  // the same chunk swizzle
   const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(p.k8 + (size_t)bh * N * D, N * D);
   const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(p.v8t + (size_t)bh * D * p.ld, D * p.ld);
   const int lw = wave & 3;
@@ -602,16 +616,16 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_pp_kernel(FwdFp8Params p) {
     const int ins = lw * IPL + i;
     const int kr = ins * 8 + (lane >> 3), kc = lane & 7;
     koff[i] = kr * D + ((kc ^ k8_swizzle(kr)) * 16);
-    const int vd = ins * 16 + (lane >> 2), vc = lane & 3;
-    voff[i] = vd * p.ld + ((vc ^ v8_swizzle(vd)) * 16);
+    const int vd = ins * (64 / CPR) + lane / CPR, vc = lane % CPR;
+    voff[i] = vd * p.ld + ((vc ^ k8_swizzle(vd)) * 16);
   }
   auto issue_k = [&](uint8_t* dst, int j) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < IPL; ++i) lds_dma16(rk, dst + (lw * IPL + i) * 1024, koff[i] + j * kBC * D);
+    for (int i = 0; i < IPL; ++i) lds_dma16(rk, dst + (lw * IPL + i) * 1024, koff[i] + j * KT * D);
   };
   auto issue_v = [&](uint8_t* dst, int j) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < IPL; ++i) lds_dma16(rv, dst + (lw * IPL + i) * 1024, voff[i] + j * kBC);
+    for (int i = 0; i < IPL; ++i) lds_dma16(rv, dst + (lw * IPL + i) * 1024, voff[i] + j * KT);
   };
 
   // running state: see fwd_fp8_kernel (power-of-two exponent reference
@@ -621,7 +635,7 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_pp_kernel(FwdFp8Params p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
   f32x16 sc[NKB];
-  i32x8 pb;               // E4M3 P^T of the last vector part (B operand of the next PV)
+  i32x8 pb[NSUB];         // E4M3 P^T of the last vector part, per 64-key half (B operands of the next PV)
   int ishift = 0, v_exp = 127;
 
   auto mfma_part = [&](int t, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
@@ -643,39 +657,45 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_pp_kernel(FwdFp8Params p) {
         }
     }
     if (t >= 1 && t <= Tw) {
-      // lane half hi reads the 32 bytes [32 hi, 32 hi + 32) of row d: keys
-      // 8w + 4hi .. +3 for w = 0..7 (the prep's order)
+      // half sub of the tile: lane half hi reads the 32 bytes [64 sub + 32 hi,
+      // +32) of row d, keys 64 sub + 8w + 4hi .. +3 for w = 0..7 (the prep's
+      // order within each aligned run of 64 keys)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int d = db * 32 + l32;
-        const uint8_t* vrow = vt + d * kBC;
-        const int sw = v8_swizzle(d);
-        const u32x4 c0 = *reinterpret_cast<const u32x4*>(vrow + (((2 * hi) ^ sw) * 16));
-        const u32x4 c1 = *reinterpret_cast<const u32x4*>(vrow + (((2 * hi + 1) ^ sw) * 16));
-        const i32x8 a = {(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3],
-                         (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
-        o[db] = mfma_fp8_32x32x64(a, pb, o[db], v_exp, 127 - 7 + ishift);
-      }
+      for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int d = db * 32 + l32;
+          const uint8_t* vrow = vt + d * KT;
+          const int sw = k8_swizzle(d);
+          const u32x4 c0 = *reinterpret_cast<const u32x4*>(vrow + (((4 * sub + 2 * hi) ^ sw) * 16));
+          const u32x4 c1 = *reinterpret_cast<const u32x4*>(vrow + (((4 * sub + 2 * hi + 1) ^ sw) * 16));
+          const i32x8 a = {(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3],
+                           (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
+          o[db] = mfma_fp8_32x32x64(a, pb[sub], o[db], v_exp, 127 - 7 + ishift);
+        }
     }
   };
 
   auto vector_part = [&](int t, float ksc, float vsc) __attribute__((always_inline)) {
     if (t >= Tw) return;
-    const int key0 = t * kBC;
+    const int key0 = t * KT;
     const float ct = cq * ksc;
     const uint32_t svb = __float_as_uint(vsc);
     const int vexp_t = (int)((svb >> 23) & 0xffu);                        // E8M0 exponent of s_V
     const float mu = __uint_as_float((svb & 0x007fffffu) | 0x3f800000u);  // s_V mantissa in [1, 2)
     const float pbias = 7.f + __builtin_amdgcn_logf(mu);
     const float inv_f = __builtin_amdgcn_rcpf(128.f * mu);
-    if ((CAUSAL && key0 + kBC - 1 > q0) || (key0 + kBC > N)) {
+    if ((CAUSAL && key0 + KT - 1 > q0) || (key0 + KT > N)) {
+      // key = key0 + 4 hi + off, off a constant per register: the key is past
+      // the row (causal) or past N iff off > lim
+      int lim = N - 1 - key0 - 4 * hi;
+      if constexpr (CAUSAL) lim = min(lim, qrow - key0 - 4 * hi);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool dead = (CAUSAL && key > qrow) || key >= N;
-          sc[kb][r] = dead ? -INFINITY : sc[kb][r];
+          const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+          sc[kb][r] = off > lim ? -INFINITY : sc[kb][r];
         }
     }
     float mx = -INFINITY;
@@ -689,16 +709,16 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_pp_kernel(FwdFp8Params p) {
     if (t == 0) m_base = (m_ref == -INFINITY) ? 0.f : m_ref;
     float shift = (m_ref == -INFINITY) ? 0.f : m_ref - m_base;
     const float moff = ((m_ref == -INFINITY) ? 0.f : m_ref) - pbias;
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+    float ls[4] = {-0.f, -0.f, -0.f, -0.f};  // x + -0 = x: the first adds fold away
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
+    for (int w = 0; w < 8 * NSUB; ++w) {
       const int kb = w >> 2, r = 4 * (w & 3);
       const float e0 = exp2_fast(__builtin_fmaf(sc[kb][r], ct, -moff));  // P * 2^7 * mu
       const float e1 = exp2_fast(__builtin_fmaf(sc[kb][r + 1], ct, -moff));
       const float e2 = exp2_fast(__builtin_fmaf(sc[kb][r + 2], ct, -moff));
       const float e3 = exp2_fast(__builtin_fmaf(sc[kb][r + 3], ct, -moff));
       ls[w & 3] += (e0 + e1) + (e2 + e3);
-      pb[w] = (int)cvt_e4m3x4(e0, e1, e2, e3);
+      pb[w >> 3][w & 7] = (int)cvt_e4m3x4(e0, e1, e2, e3);
     }
     const float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
     // rare: scores grew by more than 2^64 over the first tile's; move the base
@@ -724,7 +744,7 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_pp_kernel(FwdFp8Params p) {
     // requests, so no wait inside a part ever drains a tile request
     const float ksc = ks_next, vsc = vs_next;
     {
-      const int sb = min(((t + 1) * kBC) >> 7, nb - 1);
+      const int sb = min(t + 1, nb - 1);  // one scale block per tile
       ks_next = ks[sb];
       vs_next = vs[sb];
     }
@@ -747,8 +767,8 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_pp_kernel(FwdFp8Params p) {
     issue_k(Ks0, 0);
     issue_k(Ks1, 1);
     issue_v(Vs0, 0);
-    static_assert(2 * IPL == 4, "the wait below counts the 4 requests of stage 1");
-    __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4); expcnt, lgkmcnt left open
+    static_assert(2 * IPL < 16, "the wait below encodes the requests of stage 1 in 4 bits");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * IPL));  // vmcnt(2 IPL); expcnt, lgkmcnt left open
   } else {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   }
@@ -794,13 +814,20 @@ hipError_t launch_fp8_prep(const Fp8PrepParams& p, int d, hipStream_t stream) {
   return hipGetLastError();
 }
 
+bool fwd_fp8_pingpong(int N, bool causal) {
+  // the ping-pong kernel for non-causal N >= 1024 and causal N >= 4096
+  // (same-box measurements with 128-key tiles: 1.05-1.10 x the four-wave
+  // kernel non-causal from N = 1024 and causal from N = 4096; at causal
+  // N = 1024-2048 and at N = 512 it is 0.87-0.95 x, the 256-row workgroups
+  // balancing the triangular grid, or filling the chip, worse)
+  return causal ? N >= 4096 : N >= 1024;
+}
+
+int fwd_fp8_ref_block(int N, bool causal) { return fwd_fp8_pingpong(N, causal) ? kPPKeys : kBC; }
+
 hipError_t launch_fwd_fp8(const FwdFp8Params& p, int d, bool causal, hipStream_t stream) {
   if (d != 128) return hipErrorInvalidValue;
-  // the ping-pong kernel for non-causal N >= 1024 and causal N >= 4096 (same-box
-  // measurements: 1.04-1.08 x non-causal from N = 1024, 1.01 x causal at
-  // N = 4096, 0.95 x causal at N = 2048, where 256-row workgroups balance
-  // the triangular grid worse)
-  if (causal ? p.N >= 4096 : p.N >= 1024) {
+  if (fwd_fp8_pingpong(p.N, causal)) {
     const int nq = (p.N + 255) / 256;
     const unsigned grid = (unsigned)nq * (unsigned)p.B * (unsigned)p.H;
     if (causal)

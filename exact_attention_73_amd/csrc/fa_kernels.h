@@ -102,5 +102,9 @@ struct FwdFp8Params {
 };
 
 hipError_t launch_fwd_fp8(const FwdFp8Params& p, int d, bool causal, hipStream_t stream);
+// which forward kernel launch_fwd_fp8 runs, and the keys per exponent-reference
+// step it implies (the tile of that kernel)
+bool fwd_fp8_pingpong(int N, bool causal);
+int fwd_fp8_ref_block(int N, bool causal);
 
 }  // namespace fa

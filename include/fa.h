@@ -321,10 +321,23 @@ int fa_fp8_vt_ld(int N);
  *             powers of two with FA_PREP_POW2_SCALE, where mu_j = 1)
  *   o, lse  : as in fa_fwd_bf16
  *   d       : 128.
+ *
+ * The exponent reference of P (the running row max rounded up to a whole
+ * power of two) moves once per block of fa_fp8_ref_block(N, causal) keys:
+ * the kernel's key tile, which P of that block is quantised against
+ * ("Online Softmax 仍是精确合并的核心": each block rescales the running
+ * state; the block length is the kernel's choice).
  */
 int fa_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* q_scale, const float* k_scale,
                const float* v_scale, float* o, float* lse, int B, int H, int N, int d, int causal,
                float softmax_scale, void* stream);
+
+/* Keys per exponent-reference step of fa_fwd_fp8 for N keys (the key tile
+ * of the kernel it runs): 128 for non-causal N >= 1024 and causal
+ * N >= 4096, 64 otherwise; it divides the 128-row scale block.  Only the
+ * rounding of P depends on it.  FA_ERR_SHAPE for N < 1, FA_ERR_ARG for
+ * causal not 0/1.  Host only: no device work. */
+int fa_fp8_ref_block(int N, int causal);
 
 /* Static description of a status code (never NULL). */
 const char* fa_status_string(int status);

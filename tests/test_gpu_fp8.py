@@ -184,7 +184,8 @@ def _emulate_gpu_operands(q8, qs, k8, ks, v8t, vs, N, causal, sc):
     _, qh = _dequant_gpu(q8, qs, N)
     _, kh = _dequant_gpu(k8, ks, N)
     _, vh = _dequant_gpu(v8t, vs, N, transpose=True)
-    return fp8_attention_emulate(qh, kh, vh, causal=causal, scale=sc, Bc=64,
+    # the emulation moves the exponent reference on the blocks the kernel uses
+    return fp8_attention_emulate(qh, kh, vh, causal=causal, scale=sc, Bc=fa.fp8_ref_block(N, causal),
                                  v_scale=vs.cpu().numpy().astype(np.float64))
 
 
@@ -246,7 +247,7 @@ def test_fwd_fp8_rebase_on_growing_scores(gpu_lib, causal, N):
     (q8, qs), (k8, ks), (v8t, vs), o, lse = _fp8_pipeline(q, k, v, signs, "block+had", causal, softmax_scale=1.0)
     _, qh = _dequant_gpu(q8, qs, N)
     _, kh = _dequant_gpu(k8, ks, N)
-    shift = _rebase_shift(qh, kh, 1.0, causal)
+    shift = _rebase_shift(qh, kh, 1.0, causal, tile=fa.fp8_ref_block(N, causal))
     print(f"rebase N={N} causal={causal}: largest reference growth {shift:.0f} (log2 units)")
     assert shift > 64 + 8
     o_em, lse_em = _emulate_gpu_operands(q8, qs, k8, ks, v8t, vs, N, causal, 1.0)

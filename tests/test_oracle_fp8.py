@@ -163,13 +163,14 @@ def test_block_scales_invariants(per_tensor):
     assert np.all(np.abs(xh - y) <= np.maximum(np.abs(y) * 2.0 ** -4, srow * 2.0 ** -10) + 1e-12)
 
 
+@pytest.mark.parametrize("Bc", [64, 128])
 @pytest.mark.parametrize("mode", ["block+had", "block", "tensor"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8_emulate_without_rounding_is_attention(mode, causal):
+def test_fp8_emulate_without_rounding_is_attention(mode, causal, Bc):
     B, H, N, d = 1, 2, 200, 64
     q, k, v = (RNG.standard_normal((B, H, N, d)) for _ in range(3))
     signs = RNG.choice([-1, 1], (H, d))
-    o, l = fp8_emulate(q, k, v, signs=signs, mode=mode, causal=causal, Bc=64, quantize=False)
+    o, l = fp8_emulate(q, k, v, signs=signs, mode=mode, causal=causal, Bc=Bc, quantize=False)
     o_ref, l_ref = attention_ref(q, k, v, causal=causal)
     np.testing.assert_allclose(o, o_ref, atol=1e-12)
     np.testing.assert_allclose(l, l_ref, atol=1e-12)
@@ -232,6 +233,26 @@ def test_p_quantisation_worked_example_non_power_of_two_v_scale():
     o, lse = fp8_attention_emulate(qh, kh, vh, scale=1.0, Bc=2, v_scale=np.full((1, 1, 1), 3.0), block=128)
     np.testing.assert_allclose(o[0, 0, 0], [144 / 192 / 0.975, 44 / 192 / 0.975], rtol=1e-12)
     np.testing.assert_allclose(lse[0, 0, 0], np.log(3.9), rtol=1e-12)
+
+
+@pytest.mark.parametrize("Bc,pq1", [(1, 0.625 * 2.0 ** -15), (2, 2.0 ** -16)])
+def test_p_quantisation_depends_on_the_reference_block(Bc, pq1):
+    """Where the reference moves matters only below E4M3's normal range.  One
+    query, d = 1, scale 1; scores ln(1.3) - 16 ln 2 and 0, V = I.  With
+    blocks of one key the first key's reference is 2^-15 (log2 score -15.62
+    rounded up), so P = 0.65, times 2^7 = 83.2, rounds to 80 (step 8 in
+    [64, 128)): P_q = 0.625 * 2^-15 once rescaled to the second key's
+    reference 2^0.  With one block of both keys the reference is 2^0 from
+    the start: P * 2^7 = 1.3 * 2^-9 is subnormal in E4M3 (step 2^-9) and
+    rounds to 2^-9, so P_q = 2^-16.  Either way l sums the unrounded P,
+    1 + 1.3 * 2^-16, and O = (P_q, 1) / l."""
+    qh = np.ones((1, 1, 1, 1))
+    kh = np.array([np.log(1.3) - 16 * np.log(2.0), 0.0]).reshape(1, 1, 2, 1)
+    vh = np.eye(2).reshape(1, 1, 2, 2)
+    o, lse = fp8_attention_emulate(qh, kh, vh, scale=1.0, Bc=Bc, v_scale=np.ones((1, 1, 1)), block=128)
+    l = 1 + 1.3 * 2.0 ** -16
+    np.testing.assert_allclose(o[0, 0, 0], [pq1 / l, 1 / l], rtol=1e-12)
+    np.testing.assert_allclose(lse[0, 0, 0], np.log(l), rtol=1e-12)
 
 
 def test_fp8_emulate_v_scale_variants():
