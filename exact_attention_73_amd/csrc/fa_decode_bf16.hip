@@ -221,11 +221,13 @@ __global__ __launch_bounds__(DecCfg<D>::NW * 64, DecCfg<D>::MINB) void dec_bf16_
     }
     // keys past Nk, and (causal) keys after the query's last visible key
     if ((CAUSAL && key0 + TK - 1 > off) || key0 + TK > Nk) {
+      // key = key0 + 4 hi + k, k a constant per register: dead iff k > lim
+      int lim = Nk - 1 - key0 - 4 * hi;
+      if constexpr (CAUSAL) lim = min(lim, qi + off - key0 - 4 * hi);
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        const int key = key0 + 8 * (rr >> 2) + 4 * hi + (rr & 3);
-        const bool dead = (CAUSAL && key > qi + off) || key >= Nk;
-        s[rr] = dead ? -INFINITY : s[rr];
+        const int k = 8 * (rr >> 2) + (rr & 3);
+        s[rr] = k > lim ? -INFINITY : s[rr];
       }
     }
     float mx = -INFINITY;
@@ -257,7 +259,7 @@ __global__ __launch_bounds__(DecCfg<D>::NW * 64, DecCfg<D>::MINB) void dec_bf16_
     // P^T (bf16) as B operands: k-step ks covers keys 16 ks + 4 hi + 0..3 and
     // 16 ks + 8 + 4 hi + 0..3, registers 8 ks .. 8 ks + 7
     bf16x8 pb[2];
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+    float ls[4] = {-0.f, -0.f, -0.f, -0.f};  // x + -0 = x: the first adds fold away
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
       u32x4 t;

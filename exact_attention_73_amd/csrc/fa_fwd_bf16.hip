@@ -429,7 +429,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, (min_blocks<D, VARLEN>())) voi
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float mc = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb] * c;
-      float ls[4] = {0.f, 0.f, 0.f, 0.f};  // fp32 partial row sums (four short chains)
+      float ls[4] = {-0.f, -0.f, -0.f, -0.f};  // fp32 partial row sums (four short chains; x + -0 = x)
 #pragma unroll
       for (int ks = 0; ks < NPS; ++ks) {
         const int kb = ks >> 1, r0 = (ks & 1) * 8;
@@ -723,13 +723,15 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
     const int key0 = t * BC;
     const bool need_mask = (CAUSAL && key0 + BC - 1 > q0 + off) || (key0 + BC > Nk);
     if (need_mask) {
+      // as in the four-wave kernel: dead iff the register's key offset k > lim
+      int lim = Nk - 1 - key0 - 4 * hi;
+      if constexpr (CAUSAL) lim = min(lim, qrow + off - key0 - 4 * hi);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool dead = (CAUSAL && key > qrow + off) || key >= Nk;
-          sc[kb][r] = dead ? -INFINITY : sc[kb][r];
+          const int k = kb * 32 + 8 * (r >> 2) + (r & 3);
+          sc[kb][r] = k > lim ? -INFINITY : sc[kb][r];
         }
     }
     float mx = -INFINITY;
@@ -747,7 +749,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
       m_run = m_new;
     }
     const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+    float ls[4] = {-0.f, -0.f, -0.f, -0.f};  // x + -0 = x: the first adds fold away
 #pragma unroll
     for (int ks = 0; ks < NPS; ++ks) {
       const int kb = ks >> 1, r0 = (ks & 1) * 8;
