@@ -547,13 +547,16 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, (min_blocks<D, VARLEN>())) voi
 //   slot 2t:     group 0 matrix(t),  group 1 vector(t - 1)
 //   slot 2t + 1: group 0 vector(t),  group 1 matrix(t)
 // Stage t = {K_t, V_{t-1}} stays in LDS through slots 2t and 2t + 1, in a
-// ring of three slots (96 KB at d = 128; with the 64 KB output staging the
-// workgroup takes the CU's whole 160 KB).  Each group issues half of a
-// stage's direct-to-LDS loads inside its vector part: issuing a stage's 32
-// one-KB loads stalls the issuing waves for about 300 cycles (the address
-// unit takes them one after another), which inside a matrix part idles the
-// matrix core and inside one vector part lengthens the other group's slot;
-// split over both vector parts it hides beside the other group's products.
+// ring of four slots (128 KB at d = 128; after the loop each wave stages its
+// output tile in one of the ring's eight tile buffers).  Each group issues
+// half of a stage's direct-to-LDS loads inside its vector part (group 0 the
+// K tile, group 1 the V tile): issuing a stage's 32 one-KB loads stalls the
+// issuing waves for about 300 cycles (the address unit takes them one after
+// another), which inside a matrix part idles the matrix core and inside one
+// vector part lengthens the other group's slot; split over both vector parts
+// it hides beside the other group's products.  With four slots every tile
+// is requested three stages ahead and waited for at the end of a matrix
+// part, where the vector part of the other group still runs.
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
   constexpr int BC = D == 256 ? 32 : 64, NW = 8, QW = 32, BR = NW * QW;
@@ -566,17 +569,13 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
   // The ring is one LDS array: a slot's address is then a constant offset of
   // one base, which the reads' immediate offset field takes.  With one array
   // per slot the compiler kept a separate set of per-lane read addresses for
-  // each slot (about 40 more VGPRs).
-  __shared__ __attribute__((aligned(1024))) uint16_t ring[6 * BC * D];
-  uint16_t* const Ks0 = ring;
-  uint16_t* const Ks1 = ring + BC * D;
-  uint16_t* const Ks2 = ring + 2 * BC * D;
-  uint16_t* const Vs0 = ring + 3 * BC * D;
-  uint16_t* const Vs1 = ring + 4 * BC * D;
-  uint16_t* const Vs2 = ring + 5 * BC * D;
-  // O is staged through LDS where a wave's fp32 tile fits a ring slot (d = 64, 128)
+  // each slot (about 40 more VGPRs).  Slot i holds K in tile buffer i and V
+  // in tile buffer 4 + i.
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[8 * BC * D];
+  auto Ks = [&](int i) __attribute__((always_inline)) { return ring + i * BC * D; };
+  auto Vs = [&](int i) __attribute__((always_inline)) { return ring + (4 + i) * BC * D; };
+  // O is staged through LDS where a wave's fp32 tile fits a tile buffer (d = 64, 128)
   constexpr bool kStageO = QW * D * 4 <= BC * D * 2;
-  __shared__ __attribute__((aligned(1024))) float Ost[4][kStageO ? QW * D : 1];  // group 1's output staging
 
   const int BH = p.B * p.H;
   const int nq = (p.N + BR - 1) / BR;
@@ -689,7 +688,8 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
   };
   // K operand reads KL ahead of their products, transposed V reads VL ahead
   // (two per product); at d = 256 shorter leads keep the wave within 256 VGPRs
-  constexpr int KL = D == 256 ? 1 : 3, VL = D == 256 ? 2 : 4;
+  // (d = 128: 5 and 8 measured 1.00-1.04 x over 3 and 4, outputs equal)
+  constexpr int KL = D == 256 ? 1 : 5, VL = D == 256 ? 2 : 8;
   auto sched_qk = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_group_barrier(0x100, KL, 0);
 #pragma unroll
@@ -766,76 +766,68 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
     l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
 
-  // Both groups run the same sequence, group 1 one slot later: stage t is
-  // [group 0 requests stage t + 1] matrix(t) | barrier | vector(t) [group 0
-  // waits for its requests] | barrier.  Group 0's matrix(t) falls in slot 2t
-  // and group 1's in slot 2t + 1; stage t + 1 lands before slot 2t + 2, and
-  // its ring slot last served stage t - 1, which group 1 finished in slot
-  // 2t - 1.
-  // Stage s = {K_s, V_{s-1}} lives in ring slot s mod 3.  Each group
-  // requests half of stage t + 2 at the start of its vector part of stage
-  // t (group 0: K_{t+2} in slot 2t + 1, group 1: V_{t+1} in slot 2t + 2);
-  // that ring slot last held stage t - 1, which both groups finished in
-  // slots 2t - 2 and 2t - 1.  Group 0 waits for its half at the end of its
-  // vector part of stage t + 1, group 1 at the end of its matrix part of
-  // stage t + 1: both before the barrier that opens slot 2t + 4, where
-  // stage t + 2 is first read.  Requests past the last tile read zeros into
-  // a ring slot nobody reads again.
-  auto stage = [&](int t, const uint16_t* kt, const uint16_t* vt, uint16_t* k_fill, uint16_t* v_fill)
-                   __attribute__((always_inline)) {
-    mfma_part(t, kt, vt);
-    if (grp == 1) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): its half of stage t + 1
-    // phase switch: the only memory handed over is group 1's half of stage
-    // t + 1 (waited just above; the DMA writes LDS without the vector
-    // caches); the vector part touches no LDS and every K/V read of the
-    // matrix part is consumed by its product before the wave gets here, so
-    // no fence
+  // Both groups run the same sequence, group 1 one slot later: group 0's
+  // matrix(t) falls in slot 2t and its vector(t) in 2t + 1, group 1's in
+  // 2t + 1 and 2t + 2.  Stage s = {K_s, V_{s-1}} lives in ring slot s mod 4
+  // and is read by the matrix parts of slots 2s and 2s + 1.  At the start of
+  // its vector part of stage t, group 0 requests K_{t+3} and group 1 V_{t+2}
+  // (both of stage t + 3, ring slot (t - 1) mod 4, whose last reader
+  // finished in slot 2t - 1).  Each group waits for its requests at the end
+  // of its matrix part of stage t + 2 (group 0 in slot 2t + 4, group 1 in
+  // 2t + 5), before the barrier opening the slot after, so stage t + 3 is
+  // complete before slot 2t + 6 first reads it.  Requests past the last tile
+  // read zeros into a slot nobody reads again.
+  auto stage = [&](int t, int slot) __attribute__((always_inline)) {
+    mfma_part(t, Ks(slot), Vs(slot));
+    __builtin_amdgcn_sched_barrier(0);         // every product issues before the phase switch
+    __builtin_amdgcn_s_waitcnt(0x0F70 | IPL);  // vmcnt: all but this group's latest requests
+    // phase switch: the tiles waited for above are next read two slots on;
+    // the vector part touches no LDS and every K/V read of the matrix part is
+    // consumed by its product before the wave gets here, so no fence
     __builtin_amdgcn_s_barrier();
-    if (grp == 0) issue(rk, k_fill, koff, t + 2);
-    else issue(rv, v_fill, voff, t + 1);
+    if (grp == 0) issue(rk, Ks((slot + 3) & 3), koff, t + 3);
+    else issue(rv, Vs((slot + 3) & 3), voff, t + 2);
     vector_part(t);
-    if (grp == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | IPL);  // all but this part's requests
     __syncthreads();
   };
 
-  // prologue: K_0, then stage 1 = {K_1, V_0}, by group 0 (past the keys the
-  // range check returns zeros); wait for Q and K_0 only
+  // prologue: group 0 requests K_0, K_1, K_2 and waits for K_0 (and Q),
+  // group 1 requests V_0 and V_1 (past the keys the range check returns
+  // zeros); the rest is waited for by the waits above, each in time
   if (grp == 0) {
-    issue(rk, Ks0, koff, 0);
-    issue(rk, Ks1, koff, 1);
-    issue(rv, Vs1, voff, 0);
+    issue(rk, Ks(0), koff, 0);
+    issue(rk, Ks(1), koff, 1);
+    issue(rk, Ks(2), koff, 2);
     static_assert(2 * IPL <= 15, "the wait below encodes vmcnt in 4 bits");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * IPL));  // vmcnt(stage 1's requests); expcnt, lgkmcnt left open
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * IPL));  // vmcnt(K_1's and K_2's requests)
   } else {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), visible to the compiler's own wait tracking
+    issue(rv, Vs(1), voff, 0);
+    issue(rv, Vs(2), voff, 1);
   }
-  // K_0 landed (each loading wave waited for its share); stage 1 may still be
-  // in flight, so a plain barrier (the fence of __syncthreads would drain it)
-  // that the compiler may not move LDS accesses across
+  // K_0 landed (each loading wave waited for its share); later tiles may
+  // still be in flight, so a plain barrier (the fence of __syncthreads would
+  // drain them) that the compiler may not move LDS accesses across
   asm volatile("s_barrier" ::: "memory");
   if (grp == 1) __syncthreads();  // group 1 sits out slot 0
-  // stage t reads K_t and V_{t-1} from ring slot t mod 3 and fills slot
-  // (t + 2) mod 3; stage 0 peeled
-  stage(0, Ks0, Vs0, Ks2, Vs2);
-  for (int t = 1; t <= T; t += 3) {
-    stage(t, Ks1, Vs1, Ks0, Vs0);
-    if (t + 1 <= T) stage(t + 1, Ks2, Vs2, Ks1, Vs1);
-    if (t + 2 <= T) stage(t + 2, Ks0, Vs0, Ks2, Vs2);
+  for (int t = 0; t <= T; t += 4) {
+    stage(t, 0);
+    if (t + 1 <= T) stage(t + 1, 1);
+    if (t + 2 <= T) stage(t + 2, 2);
+    if (t + 3 <= T) stage(t + 3, 3);
   }
   if (grp == 0) __syncthreads();  // group 0 sits out the last slot
   __builtin_amdgcn_s_waitcnt(0x0F70);  // the last (unused) requests land before the ring is reused
   __syncthreads();
 
-  // epilogue: O / l, staged through LDS where it fits (group 0 in the ring,
-  // group 1 in its own area) and stored as whole rows; every wave is past its
-  // last ring read (the final barrier above)
+  // epilogue: O / l, staged through LDS where it fits (wave w in tile buffer
+  // w of the ring) and stored as whole rows; every wave is past its last ring
+  // read (the final barrier above)
   const float l_tot = sum_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < N && hi == 0) p.lse[lbase + qrow] = m_run * p.scale + __logf(l_tot);
   if constexpr (kStageO) {
     constexpr int CPO = D / 4;  // 16-byte chunks per fp32 row
-    float* st = wave >= 4 ? Ost[wave - 4]
-                          : reinterpret_cast<float*>(wave == 0 ? Ks0 : wave == 1 ? Ks1 : wave == 2 ? Vs0 : Vs1);
+    float* st = reinterpret_cast<float*>(ring + wave * BC * D);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
