@@ -216,6 +216,43 @@ def test_fwd_fp8_matches_emulation_of_its_operands(gpu_lib, N, causal, v_pow2):
     assert e2["rmse"] <= 3e-2 and e2["rel_rmse"] <= 0.15 and e2["cos"] >= 0.99
 
 
+@pytest.mark.parametrize("N,causal", [(512, False), (1024, False), (1024, True), (4096, True)])
+def test_fwd_fp8_reference_block_is_the_reported_one(gpu_lib, N, causal):
+    """The FP8 forward moves P's exponent reference once per block of
+    fa_fp8_ref_block(N, causal) keys.  Query row 200 scores -3.14 against keys
+    0..63 (V column 0 = 1 there) and 8 against keys 64..127 (scale 1, no
+    rotation): refreshed per 64 keys, the first keys' P * 2^7 * mu rounds as
+    a normal E4M3 value (101.0 -> 104); refreshed per 128 keys, the reference
+    already holds the later max and P * 2^7 * mu = 0.79 * 2^-9 rounds to the
+    subnormal 2^-9.  O[200, 0] then differs by about 23 % between the two
+    emulations; the kernel must match the one with the reported block."""
+    B, H, d, i0 = 1, 1, 128, 200
+    q = torch.zeros(B, H, N, d, dtype=torch.bfloat16)
+    k = torch.zeros(B, H, N, d, dtype=torch.bfloat16)
+    v = torch.zeros(B, H, N, d, dtype=torch.bfloat16)
+    q[0, 0, i0, 0] = 1.0
+    k[0, 0, :64, 0] = -3.2  # E4M3 code -176 of the block scale 8 / 448 (no rounding tie)
+    k[0, 0, 64:128, 0] = 8.0
+    v[0, 0, :64, 0] = 1.0
+    q8, qs = fa.fp8_prep(q.cuda())
+    k8, ks = fa.fp8_prep(k.cuda())
+    v8t, vs = fa.fp8_prep_v(v.cuda())
+    o, _ = fa.fwd_fp8(q8, k8, v8t, qs, ks, vs, causal=causal, softmax_scale=1.0)
+    torch.cuda.synchronize()
+    got = float(o[0, 0, i0, 0])
+    _, qh = _dequant_gpu(q8, qs, N)
+    _, kh = _dequant_gpu(k8, ks, N)
+    _, vh = _dequant_gpu(v8t, vs, N, transpose=True)
+    em = {bc: fp8_attention_emulate(qh, kh, vh, causal=causal, scale=1.0, Bc=bc,
+                                    v_scale=vs.cpu().numpy().astype(np.float64))[0][0, 0, i0, 0] for bc in (64, 128)}
+    blk = fa.fp8_ref_block(N, causal)
+    other = 64 if blk == 128 else 128
+    print(f"N={N} causal={causal}: block {blk}, kernel {got:.6e}, emulation 64: {em[64]:.6e}, 128: {em[128]:.6e}")
+    assert abs(em[128] - em[64]) > 0.15 * abs(em[blk])
+    assert abs(got - em[blk]) <= 1e-3 * abs(em[blk])
+    assert abs(got - em[other]) > 0.1 * abs(em[blk])
+
+
 def _rebase_shift(qh, kh, sc, causal, tile=64):
     """Largest growth, in log2 units, of a row's whole-number exponent
     reference ceil(max score * scale * log2 e) over the one it took at its
