@@ -61,6 +61,17 @@ def test_edge_shapes_full(gpu_lib, N, d, causal):
     _check(o, lse, o_ref, lse_ref, f"N={N} d={d} causal={causal}")
 
 
+# d = 128 lengths that take the ping-pong kernel with every residue of its
+# stage count (tiles + 1) modulo the four-slot ring: 64-key tiles 18, 19, 20, 21
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1100, 1216, 1280, 1300])
+def test_pingpong_ring_residues(gpu_lib, N, causal):
+    q, k, v = make_qkv(1, 2, N, 128, seed=2000 + N)
+    o, lse = _run(q, k, v, causal)
+    o_ref, lse_ref = attention_ref(q, k, v, causal=causal)
+    _check(o, lse, o_ref, lse_ref, f"ping-pong N={N} causal={causal}")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_standard_block(gpu_lib, causal):
     w = WORKLOADS["std"]
