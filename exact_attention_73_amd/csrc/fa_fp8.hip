@@ -540,7 +540,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
 // four-wave kernel's are 64): an FP8 product does the work of four bf16 ones
 // in twice the cycles, so 128-key tiles give each slot as many matrix cycles
 // as the bf16 kernel's 64-key slots and halve the barriers per key (measured
-// 1.06-1.10 x over 64-key tiles).  The exponent reference therefore moves
+// 1.05-1.11 x over 64-key tiles).  The exponent reference therefore moves
 // once per 128 keys (fa_fp8_ref_block).  A tile's step splits into a matrix
 // part (S_t = K_t Q^T: 8 products; O^T += V_{t-1}^T P_{t-1}^T: 8 products with
 // the per-lane E8M0 scales, two per 32 rows of d, one per 64-key half) and a
