@@ -51,8 +51,9 @@
 // cross a wave's diagonal are masked element-wise, waves whose rows all lie
 // above a tile skip its products, and the heaviest query tiles launch first.
 //
-// d = 128 batches of 1024 or more query rows (fixed-length, or packed with
-// such a longest sequence) run a second kernel, fwd_bf16_pp_kernel (below): eight waves per workgroup in two groups that
+// d = 128 batches of 1024 or more query rows and non-causal d = 64 and 128
+// batches of 512 or more (fixed-length, or packed with such a longest
+// sequence) run a second kernel, fwd_bf16_pp_kernel (below): eight waves per workgroup in two groups that
 // take turns on each SIMD's matrix core (one group's products while the
 // other group's softmax), the FA3 explainer's ping-pong scheduling mapped to
 // wave pairs of a SIMD.
@@ -536,7 +537,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, (min_blocks<D, VARLEN>())) voi
   }
 }
 
-// d = 128 with an explicit ping-pong between two wave groups (FA3 explainer,
+// d = 128 (and non-causal d = 64) with an explicit ping-pong between two wave groups (FA3 explainer,
 // section "第二层重叠：Ping-Pong Scheduling"): eight waves per workgroup,
 // 32 query rows each; waves w and w + 4 share a SIMD.  The step of tile t is
 // split into a matrix part (S_t = K_t Q^T and O += V_{t-1}^T P_{t-1}^T) and a
@@ -558,7 +559,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NW * 64, (min_blocks<D, VARLEN>())) voi
 // is requested three stages ahead and waited for at the end of a matrix
 // part, where the vector part of the other group still runs.
 template <int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
+__global__ __launch_bounds__(512, D == 64 ? 2 : 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
   constexpr int BC = D == 256 ? 32 : 64, NW = 8, QW = 32, BR = NW * QW;
   constexpr int ROWB = D * 2, CPR = D / 8;
   constexpr int INSTR = BC * ROWB / 1024;  // 1 KB wave-loads per tile
@@ -860,16 +861,20 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdBf16Params p) {
 // keep 128-row workgroups, which balance short causal grids better and leave
 // fewer idle rows (same-box measurements: ping-pong 1.03-1.10 x from N = 1024
 // up, 0.97 x at N = 512 causal; packed batches of 128-8192 rows 1.05-1.12 x).
-// The kernel is written for d = 64 and 256 too (32-key stages at 256) but
-// only d = 128 is dispatched: measured on one box, d = 64 ran 0.97-1.05 x its
-// three-workgroups-per-CU kernel, and d = 256 needs more than 256 VGPRs (O
-// 128, Q 64) and spills 12-13 in the loop (0.62-0.79 x).
-inline bool use_pingpong(const FwdBf16Params& p, bool causal) { return p.N >= 1024 || (!causal && p.N >= 512); }
+// At d = 64 (127 VGPRs and a 64 KB ring: two workgroups per CU) it takes
+// non-causal batches from 512 rows: 1.02 x at N = 512, 1.09-1.11 x from
+// N = 1024, where causal ones stay on the three-workgroups-per-CU kernel
+// (0.80-0.98 x there).  d = 256 needs more than 256 VGPRs (O 128, Q 64) and
+// spills 12-13 in the loop (0.62-0.79 x).
+inline bool use_pingpong(const FwdBf16Params& p, int d, bool causal) {
+  if (d == 64) return !causal && p.N >= 512;
+  return p.N >= 1024 || (!causal && p.N >= 512);
+}
 
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch(const FwdBf16Params& p, hipStream_t stream) {
-  if constexpr (D == 128) {
-    if (use_pingpong(p, CAUSAL)) {
+  if constexpr (D == 128 || (D == 64 && !CAUSAL)) {
+    if (use_pingpong(p, D, CAUSAL)) {
       const int nq = (p.N + 255) / 256;
       const unsigned grid = (unsigned)nq * (unsigned)p.B * (unsigned)p.H;
       if (grid == 0) return hipSuccess;
