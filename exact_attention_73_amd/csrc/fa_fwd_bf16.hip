@@ -51,9 +51,9 @@
 // cross a wave's diagonal are masked element-wise, waves whose rows all lie
 // above a tile skip its products, and the heaviest query tiles launch first.
 //
-// d = 128 batches of 1024 or more query rows and non-causal d = 64 and 128
-// batches of 512 or more (fixed-length, or packed with such a longest
-// sequence) run a second kernel, fwd_bf16_pp_kernel (below): eight waves per workgroup in two groups that
+// d = 128 batches of 1024 or more query rows (512 non-causal, or causal in
+// whole 256-row tiles) and non-causal d = 64 batches of 512 or more
+// (fixed-length, or packed with such a longest sequence) run a second kernel, fwd_bf16_pp_kernel (below): eight waves per workgroup in two groups that
 // take turns on each SIMD's matrix core (one group's products while the
 // other group's softmax), the FA3 explainer's ping-pong scheduling mapped to
 // wave pairs of a SIMD.
@@ -857,10 +857,13 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void fwd_bf16_pp_kernel(FwdBf
 }
 
 // The ping-pong kernel takes d = 128 batches whose longest sequence has at
-// least 1024 query rows (512 non-causal), fixed-length or packed; shorter ones
-// keep 128-row workgroups, which balance short causal grids better and leave
-// fewer idle rows (same-box measurements: ping-pong 1.03-1.10 x from N = 1024
-// up, 0.97 x at N = 512 causal; packed batches of 128-8192 rows 1.05-1.12 x).
+// least 1024 query rows, and from 512 rows non-causal ones and causal ones of
+// whole 256-row tiles, fixed-length or packed; the others keep 128-row
+// workgroups, which leave fewer idle rows and balance short causal grids
+// better (same-box measurements with the four-slot ring: ping-pong 1.03-1.10 x
+// from N = 1024 up, causal 1.03 x at N = 512 and 1.12 x at 768, but 0.94 x at
+// N = 640, a half-empty last tile, and 0.90 x at N = 256; packed batches of
+// 128-8192 rows 1.05-1.12 x).
 // At d = 64 (127 VGPRs and a 64 KB ring: two workgroups per CU) it takes
 // non-causal batches from 512 rows: 1.02 x at N = 512, 1.09-1.11 x from
 // N = 1024, where causal ones stay on the three-workgroups-per-CU kernel
@@ -868,7 +871,7 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void fwd_bf16_pp_kernel(FwdBf
 // spills 12-13 in the loop (0.62-0.79 x).
 inline bool use_pingpong(const FwdBf16Params& p, int d, bool causal) {
   if (d == 64) return !causal && p.N >= 512;
-  return p.N >= 1024 || (!causal && p.N >= 512);
+  return p.N >= 1024 || (p.N >= 512 && (!causal || p.N % 256 == 0));
 }
 
 template <int D, bool CAUSAL, bool VARLEN>

@@ -62,9 +62,10 @@ def test_edge_shapes_full(gpu_lib, N, d, causal):
 
 
 # d = 128 lengths that take the ping-pong kernel with every residue of its
-# stage count (tiles + 1) modulo the four-slot ring: 64-key tiles 18, 19, 20, 21
+# stage count (tiles + 1) modulo the four-slot ring: 64-key tiles 18, 19, 20,
+# 21; and the short whole-tile lengths where causal batches take it too
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("N", [1100, 1216, 1280, 1300])
+@pytest.mark.parametrize("N", [512, 768, 1100, 1216, 1280, 1300])
 def test_pingpong_ring_residues(gpu_lib, N, causal):
     q, k, v = make_qkv(1, 2, N, 128, seed=2000 + N)
     o, lse = _run(q, k, v, causal)
