@@ -375,7 +375,7 @@ int fa_fp8_prep(const void* x, void* x8, float* x_scale, const signed char* sign
   if (d != 128) return FA_ERR_HEADDIM;
   if (flags & ~(FA_PREP_TRANSPOSE | FA_PREP_PER_TENSOR | FA_PREP_POW2_SCALE)) return FA_ERR_ARG;
   if ((flags & FA_PREP_POW2_SCALE) && signs) return FA_ERR_ARG;
-  if (!aligned16(x) || !aligned16(x8) || !aligned16(x_scale)) return FA_ERR_ALIGN;
+  if (!aligned16(x) || !aligned16(x8) || !aligned16(x_scale) || (signs && !aligned16(signs))) return FA_ERR_ALIGN;
   if (int e = check_device()) return e;
 
   fa::Fp8PrepParams p;

@@ -264,7 +264,8 @@ int fa_bwd_bf16_gqa(const void* q, const void* k, const void* v, const float* o,
  *   signs   : int8 [H, d] of +1/-1, or NULL.  When given, each row is
  *             rotated, y = x diag(signs[h]) H_d / sqrt(d) with H_d the
  *             Sylvester Hadamard matrix (apply the same signs to Q and K;
- *             never to V).  NULL: y = x.
+ *             never to V).  NULL: y = x.  Device memory, 16-byte aligned
+ *             like every pointer here (FA_ERR_ALIGN otherwise).
  *   x8      : uint8 E4M3 (OCP e4m3fn) codes of y / s:
  *             [B, H, N, d] by default, or with FA_PREP_TRANSPOSE the
  *             transposed [B, H, d, ld] with ld = fa_fp8_vt_ld(N); columns

@@ -83,6 +83,7 @@ def test_fp8_validation(lib):
                                      kw.get("d", 128), kw.get("flags", 0), None)
     assert p(x=None) == -1 and p(N=0) == -2 and p(d=256) == -3 and p(flags=8) == -4 and p(x=FAKE + 2) == -5
     assert p(flags=4, signs=FAKE) == -4  # power-of-two scales are for the unrotated V operand
+    assert p(signs=FAKE + 8) == -5  # like every pointer argument
 
 
 def test_gqa_validation(lib):
