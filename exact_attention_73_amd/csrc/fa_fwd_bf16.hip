@@ -11,10 +11,10 @@
 // parallelism over batch, heads and query tiles): one workgroup of NW waves
 // per (batch, head, NW * 32 QB query rows); each wave owns QB blocks of 32
 // query rows, so every K or V operand read from LDS feeds QB matrix
-// instructions (LDS read bandwidth, not the matrix cores, is what 32 rows
-// per wave runs into).  With QB = 2 a wave needs more than 256 registers
-// and runs alone on its SIMD, so the overlap of matrix and vector work is
-// built into each wave's own instruction stream.
+// instructions.  Every head size runs QB = 1: with QB = 2 a wave needs more
+// than 256 registers and runs alone on its SIMD, which measured slower than
+// two or three waves per SIMD with one block each.  The overlap of matrix
+// and vector work is built into each wave's own instruction stream (below).
 //
 // Per wave the products are computed transposed, S^T = K Q^T and
 // O^T = V^T P^T, so that a lane owns ONE query row (column L & 31 of every
@@ -53,10 +53,11 @@
 //
 // d = 128 batches of 1024 or more query rows (512 non-causal, or causal in
 // whole 256-row tiles) and non-causal d = 64 batches of 512 or more
-// (fixed-length, or packed with such a longest sequence) run a second kernel, fwd_bf16_pp_kernel (below): eight waves per workgroup in two groups that
-// take turns on each SIMD's matrix core (one group's products while the
-// other group's softmax), the FA3 explainer's ping-pong scheduling mapped to
-// wave pairs of a SIMD.
+// (fixed-length, or packed with such a longest sequence) run a second
+// kernel, fwd_bf16_pp_kernel (below): eight waves per workgroup in two
+// groups that take turns on each SIMD's matrix core (one group's products
+// while the other group's softmax), the FA3 explainer's ping-pong
+// scheduling mapped to wave pairs of a SIMD.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
