@@ -31,9 +31,10 @@
 // produced directly as P * 2^7 * mu_j (exp2 bias) and cast to E4M3, and the
 // PV instruction's block exponents supply 2^-7 (P, times the shift) and
 // 2^e_j (V), where s_V,j = mu_j * 2^e_j.  Non-causal batches of 1024 or
-// more rows and causal ones of 4096 or more run fwd_fp8_pp_kernel instead:
+// more rows and causal ones of 8192 or more run fwd_fp8_pp_kernel instead:
 // the same arithmetic with eight waves per workgroup in two groups that take
-// turns on each SIMD's matrix core (ping-pong).
+// turns on each SIMD's matrix core (ping-pong).  Shorter causal batches run
+// the four-wave kernel with one S buffer per wave at three workgroups per CU.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -286,9 +287,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 __device__ __forceinline__ int k8_swizzle(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int v8_swizzle(int d) { return (d >> 2) & 3; }
 
+// Causal batches below the ping-pong kernel's length run this kernel with
+// one S buffer per wave and three workgroups per CU (166-168 VGPRs): a step
+// computes S_j, its softmax and its PV product in turn and the three waves
+// of a SIMD overlap each other's matrix and vector work; the vector unit,
+// which bounds the FP8 step, then has a third wave to fill its gaps (same-box
+// A/B: 1.02-1.08 x over two workgroups with the S double buffer from
+// N = 512 to 6000).  Non-causal batches keep the double buffer (with one
+// buffer the compiler spills hoisted LDS addresses there).
 template <bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
+__global__ __launch_bounds__(kThreads, CAUSAL ? 3 : 2) void fwd_fp8_kernel(FwdFp8Params p) {
   constexpr int D = 128;
+  constexpr bool ONE_S = CAUSAL;  // one S buffer per wave
   constexpr int NKB = kBC / 32;  // 2 key blocks of S^T per tile
   constexpr int NDB = D / 32;    // 4
   constexpr int NQS = D / 64;    // 2 k-steps of 64 d
@@ -412,21 +422,33 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
 
   // mx: raw row max of s_in on entry, of s_out on exit (taken at the end of
   // the step so that the S_{j+1} products stay in this step's block)
+  // With ONE_S, K_j and V_j sit in slot j % 2 and the step requests K_{j+1}
+  // and V_{j+1} into the other slot (read by the previous step, which every
+  // wave has left at the barrier), then computes S_j itself; k_this is then
+  // the tile of this step and k_next the slot to fill.
   auto step = [&](int j, f32x16 (&s_in)[NKB], f32x16 (&s_out)[NKB], float& mx, uint8_t* k_this,
-                  const uint8_t* k_next, const uint8_t* v_this, uint8_t* v_next) __attribute__((always_inline)) {
+                  uint8_t* k_next, const uint8_t* v_this, uint8_t* v_next) __attribute__((always_inline)) {
     const int key0 = j * kBC;
     wait_vmem_all();
     __syncthreads();
     // the scales of tile j arrived with the previous step's loads; fetch
     // those of tile j + 1 behind this step's DMAs
     const float ksc = ks_next, vsc = vs_next;
-    if (j + 2 < ntiles) issue_k(k_this, j + 2);
+    if constexpr (ONE_S) {
+      if (j + 1 < ntiles) issue_k(k_next, j + 1);
+    } else {
+      if (j + 2 < ntiles) issue_k(k_this, j + 2);
+    }
     if (j + 1 < ntiles) {
       issue_v(v_next, j + 1);
       ks_next = ks[(key0 + kBC) >> 7];
       vs_next = vs[(key0 + kBC) >> 7];
     }
     if (CAUSAL && key0 > q0 + kQW - 1) return;
+    if constexpr (ONE_S) {
+      qk(s_in, k_this);
+      mx = rowmax(s_in);
+    }
 
     const float ct = cq * ksc;
     const uint32_t svb = __float_as_uint(vsc);
@@ -456,7 +478,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
     float shift = (m_ref == -INFINITY) ? 0.f : m_ref - m_base;  // a whole number >= 0
     const float moff = ((m_ref == -INFINITY) ? 0.f : m_ref) - pbias;
 
-    qk(s_out, k_next);  // S_{j+1}: matrix cores, while the exps below run
+    if constexpr (!ONE_S) qk(s_out, k_next);  // S_{j+1}: matrix cores, while the exps below run
     i32x8 pb;
     float ls[4] = {-0.f, -0.f, -0.f, -0.f};  // x + -0 = x: the first adds fold away
 #pragma unroll
@@ -470,10 +492,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
       pb[w] = (int)cvt_e4m3x4(e0, e1, e2, e3);
     }
     const float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
-    // The test also reads lsum and the last S_{j+1} product (finite scores:
-    // adding 0 * s is exact), which keeps the products and the softmax in
-    // one block ahead of the branch, where the compiler interleaves them.
-    if (__any(shift + 0.f * (s_out[0][15] + s_out[NKB - 1][15]) > 64.f && lsum >= 0.f)) {
+    // The test also reads lsum and (with two S buffers) the last S_{j+1}
+    // product (finite scores: adding 0 * s is exact), which keeps the
+    // products and the softmax in one block ahead of the branch, where the
+    // compiler interleaves them.
+    const float s_dep = ONE_S ? 0.f : 0.f * (s_out[0][15] + s_out[NKB - 1][15]);
+    if (__any(shift + s_dep > 64.f && lsum >= 0.f)) {
       // rare (scores grew by more than 2^64 over the first tile's): move the
       // base so O and l stay far from the fp32 range; an exact power of two
       const float f = exp2_fast(-shift);
@@ -498,23 +522,31 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdFp8Params p) {
                        (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
       o[db] = mfma_fp8_32x32x64(a, pb, o[db], v_exp, 127 - 7 + ishift);
     }
-    mx = rowmax(s_out);
+    if constexpr (!ONE_S) mx = rowmax(s_out);
   };
 
-  f32x16 sa[NKB], sb[NKB];
-  float mx;
+  float mx = -INFINITY;
   issue_k(Ks0, 0);
   issue_v(Vs0, 0);
   ks_next = ks[0];
   vs_next = vs[0];
-  if (ntiles > 1) issue_k(Ks1, 1);
-  wait_vmem_all();
-  __syncthreads();
-  qk(sa, Ks0);
-  mx = rowmax(sa);
-  for (int j = 0; j < ntiles; j += 2) {
-    step(j, sa, sb, mx, Ks0, Ks1, Vs0, Vs1);
-    if (j + 1 < ntiles) step(j + 1, sb, sa, mx, Ks1, Ks0, Vs1, Vs0);
+  if constexpr (ONE_S) {
+    f32x16 sa[NKB];
+    for (int j = 0; j < ntiles; j += 2) {
+      step(j, sa, sa, mx, Ks0, Ks1, Vs0, Vs1);
+      if (j + 1 < ntiles) step(j + 1, sa, sa, mx, Ks1, Ks0, Vs1, Vs0);
+    }
+  } else {
+    f32x16 sa[NKB], sb[NKB];
+    if (ntiles > 1) issue_k(Ks1, 1);
+    wait_vmem_all();
+    __syncthreads();
+    qk(sa, Ks0);
+    mx = rowmax(sa);
+    for (int j = 0; j < ntiles; j += 2) {
+      step(j, sa, sb, mx, Ks0, Ks1, Vs0, Vs1);
+      if (j + 1 < ntiles) step(j + 1, sb, sa, mx, Ks1, Ks0, Vs1, Vs0);
+    }
   }
 
   const float l_tot = sum_halves(l_run);
@@ -815,12 +847,12 @@ hipError_t launch_fp8_prep(const Fp8PrepParams& p, int d, hipStream_t stream) {
 }
 
 bool fwd_fp8_pingpong(int N, bool causal) {
-  // the ping-pong kernel for non-causal N >= 1024 and causal N >= 4096
+  // the ping-pong kernel for non-causal N >= 1024 and causal N >= 8192
   // (same-box measurements with 128-key tiles: 1.05-1.10 x the four-wave
-  // kernel non-causal from N = 1024 and causal from N = 4096; at causal
-  // N = 1024-2048 and at N = 512 it is 0.87-0.95 x, the 256-row workgroups
-  // balancing the triangular grid, or filling the chip, worse)
-  return causal ? N >= 4096 : N >= 1024;
+  // kernel non-causal from N = 1024; causal against the one-buffer,
+  // three-workgroup four-wave kernel 0.95-0.96 x up to N = 6000 and
+  // 1.06 x at N = 8192 and 16384)
+  return causal ? N >= 8192 : N >= 1024;
 }
 
 int fwd_fp8_ref_block(int N, bool causal) { return fwd_fp8_pingpong(N, causal) ? kPPKeys : kBC; }
