@@ -31,7 +31,7 @@
 // produced directly as P * 2^7 * mu_j (exp2 bias) and cast to E4M3, and the
 // PV instruction's block exponents supply 2^-7 (P, times the shift) and
 // 2^e_j (V), where s_V,j = mu_j * 2^e_j.  Non-causal batches of 1024 or
-// more rows and causal ones of 8192 or more run fwd_fp8_pp_kernel instead:
+// more rows and causal ones of 4096 or more run fwd_fp8_pp_kernel instead:
 // the same arithmetic with eight waves per workgroup in two groups that take
 // turns on each SIMD's matrix core (ping-pong).  Shorter causal batches run
 // the four-wave kernel with one S buffer per wave at three workgroups per CU.
@@ -292,9 +292,9 @@ __device__ __forceinline__ int v8_swizzle(int d) { return (d >> 2) & 3; }
 // computes S_j, its softmax and its PV product in turn and the three waves
 // of a SIMD overlap each other's matrix and vector work; the vector unit,
 // which bounds the FP8 step, then has a third wave to fill its gaps (same-box
-// A/B: 1.02-1.08 x over two workgroups with the S double buffer from
-// N = 512 to 6000).  Non-causal batches keep the double buffer (with one
-// buffer the compiler spills hoisted LDS addresses there).
+// runs of 30-60 launches: 1.05-1.07 x over two workgroups with the S double
+// buffer at N = 1024-2048).  Non-causal batches keep the double buffer (with
+// one buffer the compiler spills hoisted LDS addresses there).
 template <bool CAUSAL>
 __global__ __launch_bounds__(kThreads, CAUSAL ? 3 : 2) void fwd_fp8_kernel(FwdFp8Params p) {
   constexpr int D = 128;
@@ -847,12 +847,12 @@ hipError_t launch_fp8_prep(const Fp8PrepParams& p, int d, hipStream_t stream) {
 }
 
 bool fwd_fp8_pingpong(int N, bool causal) {
-  // the ping-pong kernel for non-causal N >= 1024 and causal N >= 8192
-  // (same-box measurements with 128-key tiles: 1.05-1.10 x the four-wave
-  // kernel non-causal from N = 1024; causal against the one-buffer,
-  // three-workgroup four-wave kernel 0.95-0.96 x up to N = 6000 and
-  // 1.06 x at N = 8192 and 16384)
-  return causal ? N >= 8192 : N >= 1024;
+  // the ping-pong kernel for non-causal N >= 1024 and causal N >= 4096
+  // (same-box measurements with 128-key tiles, 30-60 launches back to back:
+  // 1.05-1.10 x the four-wave kernel non-causal from N = 1024; causal
+  // against the one-buffer, three-workgroup four-wave kernel 0.93-0.95 x at
+  // N = 1024-2048, 1.02 x at N = 4096, 1.06 x from N = 8192)
+  return causal ? N >= 4096 : N >= 1024;
 }
 
 int fwd_fp8_ref_block(int N, bool causal) { return fwd_fp8_pingpong(N, causal) ? kPPKeys : kBC; }

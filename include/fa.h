@@ -335,7 +335,7 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* q_s
 
 /* Keys per exponent-reference step of fa_fwd_fp8 for N keys (the key tile
  * of the kernel it runs): 128 for non-causal N >= 1024 and causal
- * N >= 8192, 64 otherwise; it divides the 128-row scale block.  Only the
+ * N >= 4096, 64 otherwise; it divides the 128-row scale block.  Only the
  * rounding of P depends on it.  FA_ERR_SHAPE for N < 1, FA_ERR_ARG for
  * causal not 0/1.  Host only: no device work. */
 int fa_fp8_ref_block(int N, int causal);

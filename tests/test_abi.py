@@ -50,7 +50,7 @@ def test_fp8_ref_block(lib):
     it runs (128-key tiles for long sequences, 64 otherwise), host only."""
     f = lib.fa_fp8_ref_block
     assert [f(N, 0) for N in (1, 64, 1023, 1024, 4096, 1 << 20)] == [64, 64, 64, 128, 128, 128]
-    assert [f(N, 1) for N in (1, 1024, 4096, 8191, 8192, 16384)] == [64, 64, 64, 64, 128, 128]
+    assert [f(N, 1) for N in (1, 1024, 4095, 4096, 8192, 16384)] == [64, 64, 64, 128, 128, 128]
     assert f(0, 0) == -2 and f(-5, 1) == -2 and f(64, 2) == -4
     assert all(128 % f(N, c) == 0 for N in (1, 100, 5000) for c in (0, 1))  # divides the scale block
 
